@@ -1,0 +1,56 @@
+// Internal launchers (host functions in the .hip files) used by the C ABI.
+// Each returns the HIP error of its launch(es); shapes are validated by the
+// caller before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lbq {
+
+hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, hipStream_t s);
+
+// RTN dequant-GEMV for 1 <= M <= 16 on already-rotated activations xr [M][K].
+hipError_t launch_gemv_rtn(const void *planes, const void *meta, const uint16_t *xr, uint16_t *y, int M, int K,
+                           int N, int bits, hipStream_t s);
+
+// RTN dequant-GEMM on MFMA for any M >= 1 on rotated activations xr [M][K].
+hipError_t launch_gemm_rtn(const void *planes, const void *meta, const uint16_t *xr, uint16_t *y, int M, int K,
+                           int N, int bits, hipStream_t s);
+
+// Product-VQ GEMV (M <= 16) and MFMA GEMM on rotated activations.
+hipError_t launch_gemv_pvq(const uint8_t *idx, const uint16_t *scale, const uint8_t *codebook, const uint16_t *xr,
+                           uint16_t *y, int M, int K, int N, hipStream_t s);
+hipError_t launch_gemm_pvq(const uint8_t *idx, const uint16_t *scale, const uint8_t *codebook, const uint16_t *xr,
+                           uint16_t *y, int M, int K, int N, hipStream_t s);
+
+hipError_t launch_unpack_rtn(const void *planes, int K, int N, int bits, uint8_t *codes, hipStream_t s);
+
+// MoE pieces.
+hipError_t launch_moe_route(const float *logits, int M, int E, int top_k, int32_t *ids, float *weights,
+                            int32_t *counts, int32_t *offsets, int32_t *perm, hipStream_t s);
+
+struct MoeArgs {
+  int E, hidden, ffn, top_k, M;
+  const uint8_t *bits;
+  const uint64_t *gu_plane_off, *gu_meta_off, *dn_plane_off, *dn_meta_off;
+  const uint8_t *planes, *meta;
+  const int8_t *signs_ffn;
+  const uint16_t *xr;        // [M][hidden] rotated tokens
+  const int32_t *offsets;    // [E+1]
+  const int32_t *perm;       // [M*top_k]
+  const float *weights;      // [M][top_k]
+  uint16_t *act;             // [M*top_k][ffn] rotated SwiGLU output, by assignment index
+  float *out;                // [M*top_k][hidden] expert outputs, by assignment index
+  uint16_t *y;               // [M][hidden]
+};
+hipError_t launch_moe_experts(const MoeArgs &a, hipStream_t s);
+// Dynamic LDS the expert kernels need (must stay within 64 KB).
+size_t moe_gateup_lds(int hidden);
+size_t moe_down_lds(int ffn);
+constexpr int kMoeMaxExperts = 1024;
+constexpr int kMoeMaxAssignments = 8192;
+constexpr int kMoeMaxTopK = 32;
+
+}  // namespace lbq

@@ -1,0 +1,328 @@
+// Routed-expert MoE block on the RTN decoders (routed experts chosen top-k per
+// token: Laguna-S-2.1 gridbook card, base-model line; per-expert code widths
+// in a Hadamard-rotated basis: LLaDA2.2-mini Orin Nano card, "Routed Experts").
+//
+// Passes, all on the caller's stream:
+//   1. route:   one workgroup; per token the top_k logits (ties to the lower
+//               expert id) and softmax weights over them; per-expert counts,
+//               exclusive offsets, and the assignment list grouped by expert.
+//   2. rotate:  x' = R_hidden x once per token (the rotate kernel).
+//   3. gate|up: one workgroup per (expert, 128-wide block of the ffn axis);
+//               inactive experts exit at once. It decodes the 128 gate rows and
+//               the 128 matching up rows at the expert's own width, applies
+//               SwiGLU, rounds to fp16, and rotates the 128-block with the ffn
+//               signs (the down weight was quantized in that basis), writing the
+//               rotated intermediate per assignment.
+//   4. down:    one workgroup per (expert, 128 output rows); writes the fp32
+//               expert output per assignment.
+//   5. combine: y_t = sum_j w_tj o_tj in fp32, slot order, fp16 out.
+// Nothing uses atomics on floating-point data, so repeated calls give
+// bit-identical y.
+#include "gemv_core.h"
+#include "kernels.h"
+
+namespace lbq {
+
+namespace {
+
+constexpr int kRouteThreads = 256;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxAssignments = 8192;
+constexpr int kMaxTokChunk = 8;
+
+// ------------------------------------------------------------------ router
+
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *__restrict__ logits, int M, int E,
+                                                                  int top_k, int32_t *__restrict__ ids,
+                                                                  float *__restrict__ weights,
+                                                                  int32_t *__restrict__ counts,
+                                                                  int32_t *__restrict__ offsets,
+                                                                  int32_t *__restrict__ perm) {
+  __shared__ int32_t s_ids[kMaxAssignments];
+  __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int32_t s_cur[kMaxExperts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kRouteThreads / 64;
+  constexpr int kPerLane = kMaxExperts / 64;
+
+  // 1. top-k per token, one wavefront per token.
+  for (int t = wave; t < M; t += kWaves) {
+    float v[kPerLane];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = (e < E) ? logits[static_cast<size_t>(t) * E + e] : 0.f;
+    }
+    float sel0 = 0.f, denom = 0.f;
+    float selv[32];
+    for (int r = 0; r < top_k; ++r) {
+      float bv = 0.f;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !((taken >> i) & 1u) && (bi == 0x7FFFFFFF || better(v[i], e, bv, bi))) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (r == 0) sel0 = bv;
+      selv[r] = bv;
+      if (lane == 0) s_ids[t * top_k + r] = bi;
+    }
+    for (int r = 0; r < top_k; ++r) denom += __expf(selv[r] - sel0);
+    if (lane < top_k) {
+      float mine = 0.f;
+      for (int r = 0; r < top_k; ++r)
+        if (r == lane) mine = selv[r];
+      weights[t * top_k + lane] = __expf(mine - sel0) / denom;
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) s_cnt[e] = 0;
+  __syncthreads();
+  const int MK = M * top_k;
+  for (int a = threadIdx.x; a < MK; a += kRouteThreads) {
+    ids[a] = s_ids[a];
+    atomicAdd(&s_cnt[s_ids[a]], 1);
+  }
+  __syncthreads();
+  // 2. exclusive offsets
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      offsets[e] = run;
+      s_cur[e] = run;
+      counts[e] = s_cnt[e];
+      run += s_cnt[e];
+    }
+    offsets[E] = run;
+  }
+  __syncthreads();
+  // 3. assignment list grouped by expert, increasing assignment index within an expert
+  for (int c0 = 0; c0 < MK; c0 += kRouteThreads) {
+    const int a = c0 + threadIdx.x;
+    const int n_in = min(kRouteThreads, MK - c0);
+    const int e = (a < MK) ? s_ids[a] : -1;
+    int rank = 0;
+    bool last = true;
+    if (a < MK) {
+      for (int i = 0; i < n_in; ++i) {
+        const int ei = s_ids[c0 + i];
+        if (ei == e) {
+          if (i < static_cast<int>(threadIdx.x)) ++rank;
+          else if (i > static_cast<int>(threadIdx.x)) last = false;
+        }
+      }
+      perm[s_cur[e] + rank] = a;
+    }
+    __syncthreads();
+    if (a < MK && last) s_cur[e] += rank + 1;
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ gate|up
+
+constexpr int kGuRows = 128;   // intermediate indices per workgroup (gate and up rows each)
+
+template <int BITS, int MT>
+__device__ void gateup_tile(const MoeArgs &a, int e, int ib, int first, int cnt, uint32_t *smem) {
+  constexpr int L = 16;
+  constexpr int R = kGemvThreads / L;   // rows per pass
+  const int G = a.hidden / kGroup;
+  const int Gc = G;                      // hidden fits LDS for MT <= 8 (checked by the host)
+  uint32_t *xx = smem;
+  float2 *sums = reinterpret_cast<float2 *>(xx + MT * Gc * kGroupStride);
+  float *hbuf = reinterpret_cast<float *>(sums + MT * Gc);   // [2*kGuRows][MT]
+  const int *perm = a.perm + first;
+  auto row_ptr = [&](int m) {
+    const int tok = perm[m] / a.top_k;
+    return reinterpret_cast<const uint32_t *>(a.xr) + static_cast<size_t>(tok) * (a.hidden / 2);
+  };
+  stage_groups<BITS, MT>(row_ptr, cnt, 0, G, Gc, xx, sums);
+  __syncthreads();
+  const uint4 *planes = reinterpret_cast<const uint4 *>(a.planes + a.gu_plane_off[e]);
+  const uint32_t *meta = reinterpret_cast<const uint32_t *>(a.meta + a.gu_meta_off[e]);
+  const int j = threadIdx.x % L;
+  for (int p = 0; p < (2 * kGuRows) / R; ++p) {
+    const int local = p * R + threadIdx.x / L;                 // 0..255: gate rows then up rows
+    const int row = (local < kGuRows) ? (ib * kGuRows + local) : (a.ffn + ib * kGuRows + local - kGuRows);
+    float yacc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) yacc[m] = 0.f;
+    row_partial<BITS, MT, L>(planes + static_cast<size_t>(row) * G * BITS, meta + static_cast<size_t>(row) * G, xx,
+                             sums, Gc, G, j, yacc);
+    reduce_cluster<MT, L>(yacc);
+    if (j == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) hbuf[local * MT + m] = yacc[m];
+    }
+  }
+  __syncthreads();
+  // SwiGLU, fp16 rounding, rotation of the 128-block, one wavefront per token.
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int m = wave; m < cnt; m += kGemvThreads / 64) {
+    float v[2];
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int r = 2 * lane + e2;
+      const float g = hbuf[r * MT + m], u = hbuf[(kGuRows + r) * MT + m];
+      const float act = g / (1.f + __expf(-g)) * u;
+      const float act16 = f16_bits_to_f32(f32_to_f16_bits(act));
+      v[e2] = act16 * static_cast<float>(a.signs_ffn[ib * kGuRows + r]);
+    }
+    fwht128_wave(v[0], v[1], lane);
+    const uint32_t packed = static_cast<uint32_t>(f32_to_f16_bits(v[0] * kInvSqrt128)) |
+                            (static_cast<uint32_t>(f32_to_f16_bits(v[1] * kInvSqrt128)) << 16);
+    reinterpret_cast<uint32_t *>(a.act + static_cast<size_t>(perm[m]) * a.ffn + ib * kGuRows)[lane] = packed;
+  }
+  __syncthreads();
+}
+
+template <int BITS>
+__device__ void gateup_bits(const MoeArgs &a, int e, int ib, int first, int n_e, uint32_t *smem) {
+  for (int c0 = 0; c0 < n_e; c0 += kMaxTokChunk) {
+    const int cnt = min(kMaxTokChunk, n_e - c0);
+    if (cnt == 1) gateup_tile<BITS, 1>(a, e, ib, first + c0, cnt, smem);
+    else if (cnt == 2) gateup_tile<BITS, 2>(a, e, ib, first + c0, cnt, smem);
+    else if (cnt <= 4) gateup_tile<BITS, 4>(a, e, ib, first + c0, cnt, smem);
+    else gateup_tile<BITS, 8>(a, e, ib, first + c0, cnt, smem);
+  }
+}
+
+__global__ void __launch_bounds__(kGemvThreads) moe_gateup_kernel(MoeArgs a) {
+  extern __shared__ uint32_t smem[];
+  const int nb = a.ffn / kGuRows;
+  const int e = blockIdx.x / nb, ib = blockIdx.x % nb;
+  const int first = a.offsets[e];
+  const int n_e = a.offsets[e + 1] - first;
+  if (n_e == 0) return;
+  switch (a.bits[e]) {
+    case 2: gateup_bits<2>(a, e, ib, first, n_e, smem); break;
+    case 3: gateup_bits<3>(a, e, ib, first, n_e, smem); break;
+    default: gateup_bits<4>(a, e, ib, first, n_e, smem); break;
+  }
+}
+
+// ------------------------------------------------------------------ down
+
+constexpr int kDnRows = 128;   // output rows per workgroup
+
+template <int BITS, int MT>
+__device__ void down_tile(const MoeArgs &a, int e, int rb, int first, int cnt, uint32_t *smem) {
+  constexpr int L = 8;
+  constexpr int R = kGemvThreads / L;
+  const int G = a.ffn / kGroup;
+  const int Gc = G;
+  uint32_t *xx = smem;
+  float2 *sums = reinterpret_cast<float2 *>(xx + MT * Gc * kGroupStride);
+  const int *perm = a.perm + first;
+  auto row_ptr = [&](int m) {
+    return reinterpret_cast<const uint32_t *>(a.act) + static_cast<size_t>(perm[m]) * (a.ffn / 2);
+  };
+  stage_groups<BITS, MT>(row_ptr, cnt, 0, G, Gc, xx, sums);
+  __syncthreads();
+  const uint4 *planes = reinterpret_cast<const uint4 *>(a.planes + a.dn_plane_off[e]);
+  const uint32_t *meta = reinterpret_cast<const uint32_t *>(a.meta + a.dn_meta_off[e]);
+  const int j = threadIdx.x % L;
+  for (int p = 0; p < kDnRows / R; ++p) {
+    const int row = rb * kDnRows + p * R + threadIdx.x / L;
+    float yacc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) yacc[m] = 0.f;
+    row_partial<BITS, MT, L>(planes + static_cast<size_t>(row) * G * BITS, meta + static_cast<size_t>(row) * G, xx,
+                             sums, Gc, G, j, yacc);
+    reduce_cluster<MT, L>(yacc);
+    if (j == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < cnt) a.out[static_cast<size_t>(perm[m]) * a.hidden + row] = yacc[m];
+    }
+  }
+  __syncthreads();
+}
+
+template <int BITS>
+__device__ void down_bits(const MoeArgs &a, int e, int rb, int first, int n_e, uint32_t *smem) {
+  for (int c0 = 0; c0 < n_e; c0 += kMaxTokChunk) {
+    const int cnt = min(kMaxTokChunk, n_e - c0);
+    if (cnt == 1) down_tile<BITS, 1>(a, e, rb, first + c0, cnt, smem);
+    else if (cnt == 2) down_tile<BITS, 2>(a, e, rb, first + c0, cnt, smem);
+    else if (cnt <= 4) down_tile<BITS, 4>(a, e, rb, first + c0, cnt, smem);
+    else down_tile<BITS, 8>(a, e, rb, first + c0, cnt, smem);
+  }
+}
+
+__global__ void __launch_bounds__(kGemvThreads) moe_down_kernel(MoeArgs a) {
+  extern __shared__ uint32_t smem[];
+  const int nb = a.hidden / kDnRows;
+  const int e = blockIdx.x / nb, rb = blockIdx.x % nb;
+  const int first = a.offsets[e];
+  const int n_e = a.offsets[e + 1] - first;
+  if (n_e == 0) return;
+  switch (a.bits[e]) {
+    case 2: down_bits<2>(a, e, rb, first, n_e, smem); break;
+    case 3: down_bits<3>(a, e, rb, first, n_e, smem); break;
+    default: down_bits<4>(a, e, rb, first, n_e, smem); break;
+  }
+}
+
+// ------------------------------------------------------------------ combine
+
+__global__ void __launch_bounds__(256) moe_combine_kernel(const float *__restrict__ out,
+                                                          const float *__restrict__ weights, int M, int hidden,
+                                                          int top_k, uint16_t *__restrict__ y) {
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<long>(M) * hidden) return;
+  const int t = static_cast<int>(i / hidden), n = static_cast<int>(i % hidden);
+  float acc = 0.f;
+  for (int jj = 0; jj < top_k; ++jj)
+    acc = fmaf(weights[t * top_k + jj], out[(static_cast<size_t>(t) * top_k + jj) * hidden + n], acc);
+  y[i] = f32_to_f16_bits(acc);
+}
+
+}  // namespace
+
+hipError_t launch_moe_route(const float *logits, int M, int E, int top_k, int32_t *ids, float *weights,
+                            int32_t *counts, int32_t *offsets, int32_t *perm, hipStream_t s) {
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, logits, M, E, top_k, ids, weights, counts,
+                     offsets, perm);
+  return hipGetLastError();
+}
+
+size_t moe_gateup_lds(int hidden) {
+  const int G = hidden / kGroup;
+  return static_cast<size_t>(kMaxTokChunk) * G * kStagedGroupBytes + 2 * kGuRows * kMaxTokChunk * sizeof(float);
+}
+size_t moe_down_lds(int ffn) { return static_cast<size_t>(kMaxTokChunk) * (ffn / kGroup) * kStagedGroupBytes; }
+
+hipError_t launch_moe_experts(const MoeArgs &a, hipStream_t s) {
+  hipError_t e;
+  hipLaunchKernelGGL(moe_gateup_kernel, dim3(a.E * (a.ffn / kGuRows)), dim3(kGemvThreads), moe_gateup_lds(a.hidden),
+                     s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_down_kernel, dim3(a.E * (a.hidden / kDnRows)), dim3(kGemvThreads), moe_down_lds(a.ffn), s,
+                     a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const long total = static_cast<long>(a.M) * a.hidden;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, a.out,
+                     a.weights, a.M, a.hidden, a.top_k, a.y);
+  return hipGetLastError();
+}
+
+}  // namespace lbq

@@ -188,8 +188,8 @@ def pack_planes(q: np.ndarray, bits: int) -> np.ndarray:
 
 
 def unpack_planes(planes: np.ndarray, bits: int, k: int) -> np.ndarray:
-    planes = np.asarray(planes, dtype=np.uint32)
-    n = planes.shape[0]
+    planes = np.asarray(planes).view(np.uint32)
+    n = planes.size // ((k // GROUP) * bits * 4)
     planes = planes.reshape(n, k // GROUP, bits, 4)
     j = np.arange(32, dtype=np.uint32)
     q = np.zeros((n, k // GROUP, 4, 32), dtype=np.uint32)

@@ -1,0 +1,213 @@
+"""GPU parity of the dense path through the C ABI: rotation, decoded codes,
+dequant-GEMV (M <= 16) and MFMA dequant-GEMM, RTN and product-VQ, against the
+CPU oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import lbq_oracle as O
+from _helpers import (TOL, cuda, make_pvq, make_rtn, oracle_pvq_rows, oracle_rtn_rows, sample_rows, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return cuda()
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_weight_only_amd import lbq
+    lbq.lib()
+    return lbq
+
+
+# ---------------------------------------------------------------- rotation
+
+@pytest.mark.parametrize("m,k", [(1, 128), (3, 4096), (16, 14336), (5, 17408), (64, 5120)])
+def test_rotate_matches_oracle(L, dev, m, k):
+    say(f"rotate m={m} k={k}")
+    x = synth.activations(m, k, workload=10, item=k)
+    s = synth.signs(k, workload=10, item=k)
+    got = L.rotate(to_dev(x, dev), to_dev(s, dev)).cpu().numpy().astype(np.float64)
+    want = O.rotate(x.astype(np.float64), s)
+    err = np.abs(got - want)
+    assert np.all(err <= 2.0 ** -10 * np.abs(want) + 2.0 ** -20), float(err.max())
+    assert O.rel_l2(got, want) < 5e-4
+
+
+# ---------------------------------------------------------------- codes
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 256), (130, 512), (257, 1152)])
+def test_unpacked_codes_bit_exact(L, dev, bits, n, k):
+    say(f"codes bits={bits} n={n} k={k}")
+    w, s, planes, meta, pl = make_rtn(n, k, bits, 11, n * 10 + bits)
+    got = L.unpack_codes(pl).cpu().numpy()
+    _, _, q = O.pack_rtn(w, bits, s)
+    assert np.array_equal(got, q)
+    assert np.array_equal(got, O.unpack_planes(planes.view(np.uint32), bits, k))
+
+
+def test_unpacked_codes_full_dense_down(L, dev):
+    k, n = 14336, 4096
+    say("codes full 14336x4096 2-bit")
+    w, s, planes, meta, pl = make_rtn(n, k, 2, synth.W_STACK, 3)
+    got = L.unpack_codes(pl).cpu().numpy()
+    assert np.array_equal(got, O.unpack_planes(planes.view(np.uint32), 2, k))
+    rows = sample_rows(n, 32, seed=3)
+    _, _, q = O.pack_rtn(w[rows], 2, s)
+    assert np.array_equal(got[rows], q)
+
+
+def test_pvq_codes_roundtrip(L, dev):
+    w, s, cb, idx, sc, pl = make_pvq(64, 512, 12, 1)
+    got = L.unpack_codes(pl).cpu().numpy()
+    oi, _ = O.pack_pvq(w, s, cb)
+    assert np.array_equal(got, oi)
+
+
+# ---------------------------------------------------------------- GEMV (M <= 16)
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 256), (130, 512), (257, 1024), (64, 4096)])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 13, 16])
+def test_gemv_small_shapes(L, dev, bits, n, k, m):
+    say(f"gemv bits={bits} n={n} k={k} m={m}")
+    w, s, planes, meta, pl = make_rtn(n, k, bits, 13, n + k + bits)
+    x = synth.activations(m, k, workload=13, item=m)
+    y = L.linear_forward(pl, to_dev(x, dev), path=L.PATH_GEMV).cpu().numpy().astype(np.float64)
+    want = oracle_rtn_rows(w, s, bits, x)
+    assert O.rel_l2(y, want) < TOL
+
+
+def test_gemv_single_linear_full(L, dev):
+    """The 4096x4096 2-bit single linear at M=1, every output."""
+    say("gemv single linear 4096x4096 M=1")
+    w, s, planes, meta, pl = make_rtn(4096, 4096, 2, synth.W_SINGLE, 0)
+    x = synth.activations(1, 4096, workload=synth.W_SINGLE)
+    y = L.linear_forward(pl, to_dev(x, dev)).cpu().numpy().astype(np.float64)
+    want = oracle_rtn_rows(w, s, 2, x)
+    e = O.rel_l2(y, want)
+    say(f"  rel_l2={e:.3e}")
+    assert e < TOL
+
+
+@pytest.mark.parametrize("shape", synth.DENSE_STACK_SHAPES, ids=[s[0] for s in synth.DENSE_STACK_SHAPES])
+@pytest.mark.parametrize("m", synth.DENSE_STACK_M)
+def test_gemv_dense_stack_sampled(L, dev, shape, m):
+    name, k, n = shape
+    say(f"gemv dense stack {name} k={k} n={n} m={m}")
+    w, s, planes, meta, pl = make_rtn(n, k, 2, synth.W_STACK, synth.DENSE_STACK_SHAPES.index(shape))
+    x = synth.activations(m, k, workload=synth.W_STACK, item=m)
+    y = L.linear_forward(pl, to_dev(x, dev)).cpu().numpy().astype(np.float64)
+    rows = sample_rows(n, 64, seed=m)
+    want = oracle_rtn_rows(w, s, 2, x, rows)
+    e = O.rel_l2(y[:, rows], want)
+    say(f"  rel_l2={e:.3e}")
+    assert e < TOL
+
+
+# ---------------------------------------------------------------- MFMA GEMM
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("n,k", [(1, 128), (70, 256), (130, 512), (64, 1024)])
+@pytest.mark.parametrize("m", [1, 17, 33, 64, 100, 129])
+def test_gemm_small_shapes(L, dev, bits, n, k, m):
+    say(f"gemm bits={bits} n={n} k={k} m={m}")
+    w, s, planes, meta, pl = make_rtn(n, k, bits, 14, n + k + bits)
+    x = synth.activations(m, k, workload=14, item=m)
+    y = L.linear_forward(pl, to_dev(x, dev), path=L.PATH_GEMM).cpu().numpy().astype(np.float64)
+    want = oracle_rtn_rows(w, s, bits, x)
+    assert O.rel_l2(y, want) < TOL
+
+
+@pytest.mark.parametrize("swap", [False, True], ids=["gu2_dn3", "gu3_dn2"])
+@pytest.mark.parametrize("m", synth.FFN_SWEEP["M"])
+def test_ffn_sweep_sampled(L, dev, swap, m):
+    """5120 -> 17408 gate|up and 17408 -> 5120 down at mixed 2/3-bit widths;
+    M = 1, 8 run the GEMV, M = 64, 256 the MFMA GEMM."""
+    cfg = synth.FFN_SWEEP
+    b_gu, b_dn = (cfg["bits_gu"], cfg["bits_dn"]) if not swap else (cfg["bits_dn"], cfg["bits_gu"])
+    for (k, n, bits, item) in [(cfg["K_gu"], cfg["N_gu"], b_gu, 1), (cfg["N_gu"], cfg["K_gu"], b_dn, 2)]:
+        say(f"ffn sweep k={k} n={n} bits={bits} m={m}")
+        w, s, planes, meta, pl = make_rtn(n, k, bits, synth.W_FFN, item)
+        x = synth.activations(m, k, workload=synth.W_FFN, item=m)
+        y = L.linear_forward(pl, to_dev(x, dev)).cpu().numpy().astype(np.float64)
+        rows = sample_rows(n, 48, seed=m + item)
+        want = oracle_rtn_rows(w, s, bits, x, rows)
+        e = O.rel_l2(y[:, rows], want)
+        say(f"  rel_l2={e:.3e}")
+        assert e < TOL
+
+
+def test_gemv_and_gemm_agree(L, dev):
+    w, s, planes, meta, pl = make_rtn(512, 2048, 2, 15, 1)
+    x = to_dev(synth.activations(16, 2048, workload=15), dev)
+    a = L.linear_forward(pl, x, path=L.PATH_GEMV).cpu().numpy().astype(np.float64)
+    b = L.linear_forward(pl, x, path=L.PATH_GEMM).cpu().numpy().astype(np.float64)
+    assert O.rel_l2(a, b) < 1e-3
+
+
+def test_repeat_calls_bit_identical(L, dev):
+    w, s, planes, meta, pl = make_rtn(1024, 4096, 3, 15, 2)
+    for m in (1, 64):
+        x = to_dev(synth.activations(m, 4096, workload=15, item=m), dev)
+        a = L.linear_forward(pl, x).cpu().numpy()
+        b = L.linear_forward(pl, x).cpu().numpy()
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_zero_tokens_is_noop(L, dev):
+    import torch
+
+    w, s, planes, meta, pl = make_rtn(64, 256, 2, 15, 3)
+    x = torch.empty((0, 256), dtype=torch.float16, device=dev)
+    y = L.linear_forward(pl, x)
+    assert y.shape == (0, 64)
+
+
+def test_zero_weights_give_zero_output(L, dev):
+    """All-zero weights pack to codes 0 with the degenerate scale 1. The GEMM
+    sums exact integers (q - z) and returns exact zeros; the GEMV removes the
+    fp16 1.0 it inserts codes into with per-group activation sums, so it leaves
+    an fp32 cancellation residue of a few ulps of those sums (|x| ~ 1 here)."""
+    from bit_weight_only_amd import lbq
+
+    k, n = 256, 32
+    s = synth.signs(k, workload=15)
+    planes, meta = lbq.pack(np.zeros((n, k), np.float32), 2, s)
+    pl = lbq.PackedLinear.from_host(planes, meta, s, k, n, 2)
+    x = to_dev(synth.activations(3, k, workload=15), dev)
+    y = L.linear_forward(pl, x, path=L.PATH_GEMM).cpu().numpy()
+    assert np.all(y == 0)
+    y = L.linear_forward(pl, x, path=L.PATH_GEMV).cpu().numpy().astype(np.float64)
+    assert np.abs(y).max() < 2e-3
+
+
+# ---------------------------------------------------------------- product-VQ
+
+@pytest.mark.parametrize("n,k", [(1, 128), (130, 512), (257, 1024)])
+@pytest.mark.parametrize("m,path", [(1, 1), (3, 1), (16, 1), (1, 2), (40, 2), (64, 2), (129, 2)])
+def test_pvq_small_shapes(L, dev, n, k, m, path):
+    say(f"pvq n={n} k={k} m={m} path={path}")
+    w, s, cb, idx, sc, pl = make_pvq(n, k, 16, n + k)
+    x = synth.activations(m, k, workload=16, item=m)
+    y = L.linear_forward(pl, to_dev(x, dev), path=path).cpu().numpy().astype(np.float64)
+    want = oracle_pvq_rows(w, s, cb, x)
+    assert O.rel_l2(y, want) < TOL
+
+
+@pytest.mark.parametrize("m", synth.PVQ_LINEAR["M"])
+def test_pvq_linear_sampled(L, dev, m):
+    cfg = synth.PVQ_LINEAR
+    say(f"pvq 4096x14336 m={m}")
+    w, s, cb, idx, sc, pl = make_pvq(cfg["N"], cfg["K"], synth.W_PVQ, 0)
+    x = synth.activations(m, cfg["K"], workload=synth.W_PVQ, item=m)
+    y = L.linear_forward(pl, to_dev(x, dev)).cpu().numpy().astype(np.float64)
+    rows = sample_rows(cfg["N"], 48, seed=m)
+    want = oracle_pvq_rows(w, s, cb, x, rows)
+    e = O.rel_l2(y[:, rows], want)
+    say(f"  rel_l2={e:.3e}")
+    assert e < TOL
