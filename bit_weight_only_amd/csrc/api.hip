@@ -33,7 +33,10 @@ lbq_status check_weight(const lbq_weight *w) {
   return LBQ_OK;
 }
 
-size_t linear_ws_bytes(int M, int K) { return round_up(static_cast<size_t>(M) * K * 2, kAlign); }
+size_t linear_ws_bytes(int M, int K) {
+  // the rotated activations
+  return round_up(static_cast<size_t>(M) * K * 2, kAlign);
+}
 
 }  // namespace
 
@@ -110,10 +113,13 @@ lbq_status lbq_linear_forward_path(const lbq_weight *w, const uint16_t *x, int32
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return LBQ_ERR_ALIGN;
   if (ws_bytes < linear_ws_bytes(M, w->K)) return LBQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 16);
+  // One or two tokens on short rows: rotation fused into the decoder, one launch.
+  if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_fold_supported(M, w->K) && aligned16(w->signs))
+    return hip_status(launch_gemv_fold(w->planes, w->meta, x, w->signs, y, M, w->K, w->N, w->bits, 0, 0, 0, s));
   uint16_t *xr = static_cast<uint16_t *>(ws);
   hipError_t e = launch_rotate(x, M, w->K, w->signs, xr, s);
   if (e != hipSuccess) return LBQ_ERR_HIP;
-  const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 16);
   if (w->format == LBQ_FMT_RTN_PLANES) {
     if (gemv) return hip_status(launch_gemv_rtn(w->planes, w->meta, xr, y, M, w->K, w->N, w->bits, s));
     return hip_status(launch_gemm_rtn(w->planes, w->meta, xr, y, M, w->K, w->N, w->bits, s));

@@ -18,8 +18,20 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 128;
 
+// Single-instruction bit operations. Written as (non-volatile) inline asm so the
+// compiler keeps one v_bfi_b32 per merged word and one v_and_or_b32 per decoded
+// slot, with the masks in SGPRs and the fp16 constant in a VGPR; left to
+// itself it fuses the merge into every slot extraction and splits the OR of the
+// constant into a second instruction.
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
-  return (a & mask) | (b & ~mask);
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(c));
+  return r;
 }
 
 // Two 1-bit planes of one 32-code word column -> two words of 2-bit fields.
@@ -63,22 +75,23 @@ __device__ __forceinline__ void decode_slots2(uint32_t p0, uint32_t p1, uint32_t
   uint32_t e, o;
   merge2(p0, p1, e, o);
   const uint32_t e6 = e >> 6, o6 = o >> 6;
-  h[0] = (e & 0x00030003u) | kOne2;
-  h[1] = (o & 0x00030003u) | kOne2;
-  h[2] = (e & 0x000C000Cu) | kOne2;
-  h[3] = (o & 0x000C000Cu) | kOne2;
-  h[4] = (e & 0x00300030u) | kOne2;
-  h[5] = (o & 0x00300030u) | kOne2;
-  h[6] = (e & 0x00C000C0u) | kOne2;
-  h[7] = (o & 0x00C000C0u) | kOne2;
-  h[8] = (e & 0x03000300u) | kOne2;
-  h[9] = (o & 0x03000300u) | kOne2;
-  h[10] = (e6 & 0x00300030u) | kOne2;
-  h[11] = (o6 & 0x00300030u) | kOne2;
-  h[12] = (e6 & 0x00C000C0u) | kOne2;
-  h[13] = (o6 & 0x00C000C0u) | kOne2;
-  h[14] = (e6 & 0x03000300u) | kOne2;
-  h[15] = (o6 & 0x03000300u) | kOne2;
+  const uint32_t one = kOne2;
+  h[0] = and_or(e, 0x00030003u, one);
+  h[1] = and_or(o, 0x00030003u, one);
+  h[2] = and_or(e, 0x000C000Cu, one);
+  h[3] = and_or(o, 0x000C000Cu, one);
+  h[4] = and_or(e, 0x00300030u, one);
+  h[5] = and_or(o, 0x00300030u, one);
+  h[6] = and_or(e, 0x00C000C0u, one);
+  h[7] = and_or(o, 0x00C000C0u, one);
+  h[8] = and_or(e, 0x03000300u, one);
+  h[9] = and_or(o, 0x03000300u, one);
+  h[10] = and_or(e6, 0x00300030u, one);
+  h[11] = and_or(o6, 0x00300030u, one);
+  h[12] = and_or(e6, 0x00C000C0u, one);
+  h[13] = and_or(o6, 0x00C000C0u, one);
+  h[14] = and_or(e6, 0x03000300u, one);
+  h[15] = and_or(o6, 0x03000300u, one);
 }
 // Class of each 2-bit slot (index into scale 2^(10 - 2*cls)).
 __host__ __device__ constexpr int slot_class2(int c) {
@@ -95,10 +108,11 @@ __device__ __forceinline__ void decode_slots_nib(const uint32_t *p, uint32_t h[1
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t w = n[r], w8 = n[r] >> 8;
-    h[r] = (w & 0x000F000Fu) | kOne2;
-    h[4 + r] = (w & 0x00F000F0u) | kOne2;
-    h[8 + r] = (w8 & 0x000F000Fu) | kOne2;
-    h[12 + r] = (w8 & 0x00F000F0u) | kOne2;
+    const uint32_t one = kOne2;
+    h[r] = and_or(w, 0x000F000Fu, one);
+    h[4 + r] = and_or(w, 0x00F000F0u, one);
+    h[8 + r] = and_or(w8, 0x000F000Fu, one);
+    h[12 + r] = and_or(w8, 0x00F000F0u, one);
   }
 }
 __host__ __device__ constexpr int slot_class_nib(int c) { return (c >> 2) & 1; }
@@ -118,6 +132,12 @@ template <int BITS>
 __host__ __device__ constexpr int slot_class(int c) {
   if constexpr (BITS == 2) return slot_class2(c);
   else return slot_class_nib(c);
+}
+template <int BITS>
+__host__ __device__ constexpr int first_slot_of_class(int cls) {
+  for (int c = 0; c < 16; ++c)
+    if (slot_class<BITS>(c) == cls) return c;
+  return -1;
 }
 template <int BITS>
 __host__ __device__ constexpr float class_weight(int cls) {

@@ -99,7 +99,11 @@ __device__ __forceinline__ void row_partial(const uint4 *__restrict__ prow, cons
           xv[4 * i + 3] = v.w;
         }
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[m][slot_class<BITS>(c)] = dot2(h[c], xv[c], acc[m][slot_class<BITS>(c)]);
+        for (int c = 0; c < 16; ++c) {
+          const int cls = slot_class<BITS>(c);
+          // the first slot of a class in the first word starts its accumulator
+          acc[m][cls] = dot2(h[c], xv[c], (w == 0 && c == first_slot_of_class<BITS>(cls)) ? 0.f : acc[m][cls]);
+        }
       }
     }
     const float sc = f16_bits_to_f32(mt & 0xFFFFu);

@@ -15,6 +15,15 @@ hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, u
 hipError_t launch_gemv_rtn(const void *planes, const void *meta, const uint16_t *xr, uint16_t *y, int M, int K,
                            int N, int bits, hipStream_t s);
 
+// RTN dequant-GEMV on raw activations x [M][K] (M = 1 or 2) with the rotation
+// in the kernel's prologue: one launch, no workspace. signs must be 16-byte
+// aligned. gemv_fold_supported says where this path is the faster one;
+// lanes <= 0 picks the launch shape (gemv_fold_shape).
+bool gemv_fold_supported(int M, int K);
+void gemv_fold_shape(int M, int K, int N, int &lanes, int &rb, int &grid_cap);
+hipError_t launch_gemv_fold(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs, uint16_t *y,
+                            int M, int K, int N, int bits, int lanes, int rb, int grid_cap, hipStream_t s);
+
 // RTN dequant-GEMM on MFMA for any M >= 1 on rotated activations xr [M][K].
 hipError_t launch_gemm_rtn(const void *planes, const void *meta, const uint16_t *xr, uint16_t *y, int M, int K,
                            int N, int bits, hipStream_t s);

@@ -143,7 +143,9 @@ lbq_status lbq_pack(const float *W, int32_t K, int32_t N, int32_t bits, int32_t 
 lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
 
 /* y[M][N] (fp16) = x[M][K] (fp16) W_hat^T, W_hat the weight w decodes to.
- * Rotates x into the workspace, then runs the dequant-GEMV (M <= 16) or the
+ * The activation rotation runs either inside the GEMV's prologue (one or two
+ * tokens on rows of up to 8192 / 4096 inputs, signs 16-byte aligned) or as its
+ * own launch into the workspace, followed by the dequant-GEMV (M <= 16) or the
  * MFMA dequant-GEMM (M >= 17). Accumulation is fp32. */
 lbq_status lbq_linear_forward(const lbq_weight *w, const uint16_t *x, int32_t M,
                               uint16_t *y, void *ws, size_t ws_bytes, void *stream);

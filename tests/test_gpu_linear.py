@@ -82,6 +82,30 @@ def test_gemv_small_shapes(L, dev, bits, n, k, m):
     assert O.rel_l2(y, want) < TOL
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("n,k", [(257, 4096), (130, 5120), (67, 8192)])
+@pytest.mark.parametrize("m", [1, 2])
+def test_gemv_fused_and_staged_rotation_agree(L, dev, bits, n, k, m):
+    """One or two tokens normally rotate inside the GEMV prologue; signs that
+    are not 16-byte aligned send the same call through the separate rotation
+    launch and the staged GEMV. Both must match the oracle and each other."""
+    import torch
+
+    say(f"gemv fused/staged bits={bits} n={n} k={k} m={m}")
+    w, s, planes, meta, pl = make_rtn(n, k, bits, 16, n + k + bits)
+    x = to_dev(synth.activations(m, k, workload=16, item=m), dev)
+    a = L.linear_forward(pl, x).cpu().numpy().astype(np.float64)
+    buf = torch.zeros(k + 16, dtype=torch.int8, device=dev)
+    buf[1:1 + k].copy_(pl.signs)
+    pl_odd = L.PackedLinear(k, n, bits, L.FMT_RTN_PLANES, pl.planes, pl.meta, buf[1:1 + k])
+    assert pl_odd.signs.data_ptr() % 16 == 1
+    b = L.linear_forward(pl_odd, x).cpu().numpy().astype(np.float64)
+    want = oracle_rtn_rows(w, s, bits, x.cpu().numpy())
+    assert O.rel_l2(a, want) < TOL
+    assert O.rel_l2(b, want) < TOL
+    assert O.rel_l2(a, b) < 1e-3
+
+
 def test_gemv_single_linear_full(L, dev):
     """The 4096x4096 2-bit single linear at M=1, every output."""
     say("gemv single linear 4096x4096 M=1")
