@@ -33,9 +33,11 @@ lbq_status check_weight(const lbq_weight *w) {
   return LBQ_OK;
 }
 
-size_t linear_ws_bytes(int M, int K) {
-  // the rotated activations
-  return round_up(static_cast<size_t>(M) * K * 2, kAlign);
+size_t linear_ws_bytes(int M, int K, int N) {
+  // the rotated activations, their per-(group, token) sums, then the GEMM's
+  // split-K partial tiles and counters
+  return round_up(static_cast<size_t>(M) * K * 2, kAlign) + round_up(static_cast<size_t>(M) * (K / 128) * 8, kAlign) +
+         gemm_scratch_bytes(gemm_plan(M, K, N));
 }
 
 }  // namespace
@@ -97,7 +99,7 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes) {
   lbq_status st = check_weight(w);
   if (st != LBQ_OK) return st;
   if (M < 0) return LBQ_ERR_SHAPE;
-  *bytes = linear_ws_bytes(M, w->K);
+  *bytes = linear_ws_bytes(M, w->K, w->N);
   return LBQ_OK;
 }
 
@@ -111,24 +113,33 @@ lbq_status lbq_linear_forward_path(const lbq_weight *w, const uint16_t *x, int32
   if (M == 0) return LBQ_OK;
   if (!x || !y || !ws) return LBQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return LBQ_ERR_ALIGN;
-  if (ws_bytes < linear_ws_bytes(M, w->K)) return LBQ_ERR_WORKSPACE;
+  if (ws_bytes < linear_ws_bytes(M, w->K, w->N)) return LBQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 16);
+  // the MFMA GEMM's decode costs the same at 4 tokens as at 16; below that the
+  // VALU GEMV is faster
+  const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 3);
   // One or two tokens on short rows: rotation fused into the decoder, one launch.
   if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_fold_supported(M, w->K) && aligned16(w->signs))
     return hip_status(launch_gemv_fold(w->planes, w->meta, x, w->signs, y, M, w->K, w->N, w->bits, 0, 0, 0, s));
   uint16_t *xr = static_cast<uint16_t *>(ws);
+  if (!gemv) {
+    // MFMA GEMM: rotation into the folded order (clearing the split-K counters), then the GEMM
+    const GemmPlan gp = gemm_plan(M, w->K, w->N);
+    float2 *sums =
+        reinterpret_cast<float2 *>(static_cast<uint8_t *>(ws) + round_up(static_cast<size_t>(M) * w->K * 2, kAlign));
+    void *scratch = reinterpret_cast<uint8_t *>(sums) + round_up(static_cast<size_t>(M) * (w->K / 128) * 8, kAlign);
+    if (launch_rotate_folded(x, M, w->K, w->signs, w->bits, xr, sums, gemm_counter_ptr(gp, scratch),
+                             gemm_counters(gp), s) != hipSuccess)
+      return LBQ_ERR_HIP;
+    return hip_status(launch_gemm(gp, w->format, w->bits, w->planes, w->meta,
+                                  static_cast<const uint8_t *>(w->codebook), xr, sums, y, M, w->K, w->N, scratch, s));
+  }
   hipError_t e = launch_rotate(x, M, w->K, w->signs, xr, s);
   if (e != hipSuccess) return LBQ_ERR_HIP;
-  if (w->format == LBQ_FMT_RTN_PLANES) {
-    if (gemv) return hip_status(launch_gemv_rtn(w->planes, w->meta, xr, y, M, w->K, w->N, w->bits, s));
-    return hip_status(launch_gemm_rtn(w->planes, w->meta, xr, y, M, w->K, w->N, w->bits, s));
-  }
-  const uint8_t *idx = static_cast<const uint8_t *>(w->planes);
-  const uint16_t *sc = static_cast<const uint16_t *>(w->meta);
-  const uint8_t *cb = static_cast<const uint8_t *>(w->codebook);
-  if (gemv) return hip_status(launch_gemv_pvq(idx, sc, cb, xr, y, M, w->K, w->N, s));
-  return hip_status(launch_gemm_pvq(idx, sc, cb, xr, y, M, w->K, w->N, s));
+  if (w->format == LBQ_FMT_RTN_PLANES)
+    return hip_status(launch_gemv_rtn(w->planes, w->meta, xr, y, M, w->K, w->N, w->bits, s));
+  return hip_status(launch_gemv_pvq(static_cast<const uint8_t *>(w->planes), static_cast<const uint16_t *>(w->meta),
+                                    static_cast<const uint8_t *>(w->codebook), xr, y, M, w->K, w->N, s));
 }
 
 lbq_status lbq_linear_forward(const lbq_weight *w, const uint16_t *x, int32_t M, uint16_t *y, void *ws,

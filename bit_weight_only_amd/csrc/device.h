@@ -63,35 +63,45 @@ __device__ __forceinline__ void merge_nibbles(const uint32_t *p, uint32_t n[4]) 
 // the exact fp16 value 1 + q * 2^(m - 10).
 constexpr uint32_t kOne2 = 0x3C003C00u;
 
+// fp16 2^(10 - m) in both halves. OR-ing a code q into mantissa bits m.. of it
+// gives the exact fp16 value 2^(10 - m) + q: the code with a class-dependent
+// offset and weight 1 in every class.
+__host__ __device__ constexpr uint32_t biased_one2(int m) {
+  return static_cast<uint32_t>(25 - m) << 10 | static_cast<uint32_t>(25 - m) << 26;
+}
+
 // Decode one 32-code word column into 16 half2 "slots". Slot c holds the codes
 // of positions c and c + 16 (lo, hi half) encoded as 1 + q * 2^(m(c) - 10), with
-// m(c) the class of the slot. The activations are staged in the same slot
-// order: slot c pairs x[c] with x[c + 16].
+// m(c) the class of the slot (BIASED: as 2^(10 - m(c)) + q). The activations
+// are staged in the same slot order: slot c pairs x[c] with x[c + 16].
 //
 // 2-bit: slot 2p / 2p+1 comes from field p of e / o; fields 0..4 sit at
 // m = 0, 2, 4, 6, 8 directly, fields 5..7 after a shift by 6 at m = 4, 6, 8.
 // Class index (m / 2): {0,0,1,1,2,2,3,3,4,4,2,2,3,3,4,4}.
+template <bool BIASED = false>
 __device__ __forceinline__ void decode_slots2(uint32_t p0, uint32_t p1, uint32_t h[16]) {
   uint32_t e, o;
   merge2(p0, p1, e, o);
   const uint32_t e6 = e >> 6, o6 = o >> 6;
-  const uint32_t one = kOne2;
-  h[0] = and_or(e, 0x00030003u, one);
-  h[1] = and_or(o, 0x00030003u, one);
-  h[2] = and_or(e, 0x000C000Cu, one);
-  h[3] = and_or(o, 0x000C000Cu, one);
-  h[4] = and_or(e, 0x00300030u, one);
-  h[5] = and_or(o, 0x00300030u, one);
-  h[6] = and_or(e, 0x00C000C0u, one);
-  h[7] = and_or(o, 0x00C000C0u, one);
-  h[8] = and_or(e, 0x03000300u, one);
-  h[9] = and_or(o, 0x03000300u, one);
-  h[10] = and_or(e6, 0x00300030u, one);
-  h[11] = and_or(o6, 0x00300030u, one);
-  h[12] = and_or(e6, 0x00C000C0u, one);
-  h[13] = and_or(o6, 0x00C000C0u, one);
-  h[14] = and_or(e6, 0x03000300u, one);
-  h[15] = and_or(o6, 0x03000300u, one);
+  const uint32_t c0 = BIASED ? biased_one2(0) : kOne2, c2 = BIASED ? biased_one2(2) : kOne2;
+  const uint32_t c4 = BIASED ? biased_one2(4) : kOne2, c6 = BIASED ? biased_one2(6) : kOne2;
+  const uint32_t c8 = BIASED ? biased_one2(8) : kOne2;
+  h[0] = and_or(e, 0x00030003u, c0);
+  h[1] = and_or(o, 0x00030003u, c0);
+  h[2] = and_or(e, 0x000C000Cu, c2);
+  h[3] = and_or(o, 0x000C000Cu, c2);
+  h[4] = and_or(e, 0x00300030u, c4);
+  h[5] = and_or(o, 0x00300030u, c4);
+  h[6] = and_or(e, 0x00C000C0u, c6);
+  h[7] = and_or(o, 0x00C000C0u, c6);
+  h[8] = and_or(e, 0x03000300u, c8);
+  h[9] = and_or(o, 0x03000300u, c8);
+  h[10] = and_or(e6, 0x00300030u, c4);
+  h[11] = and_or(o6, 0x00300030u, c4);
+  h[12] = and_or(e6, 0x00C000C0u, c6);
+  h[13] = and_or(o6, 0x00C000C0u, c6);
+  h[14] = and_or(e6, 0x03000300u, c8);
+  h[15] = and_or(o6, 0x03000300u, c8);
 }
 // Class of each 2-bit slot (index into scale 2^(10 - 2*cls)).
 __host__ __device__ constexpr int slot_class2(int c) {
@@ -101,18 +111,18 @@ __host__ __device__ constexpr int slot_class2(int c) {
 // 3/4-bit: slot 4p + r comes from nibble word r; nibbles p and p+4 of the word
 // (for p = 0, 1) or of the word shifted by 8 (p = 2, 3). m = 0 for even p,
 // m = 4 for odd p. Class index: 0 (m = 0) or 1 (m = 4).
-template <int BITS>
+template <int BITS, bool BIASED = false>
 __device__ __forceinline__ void decode_slots_nib(const uint32_t *p, uint32_t h[16]) {
   uint32_t n[4];
   merge_nibbles<BITS>(p, n);
+  const uint32_t c0 = BIASED ? biased_one2(0) : kOne2, c4 = BIASED ? biased_one2(4) : kOne2;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t w = n[r], w8 = n[r] >> 8;
-    const uint32_t one = kOne2;
-    h[r] = and_or(w, 0x000F000Fu, one);
-    h[4 + r] = and_or(w, 0x00F000F0u, one);
-    h[8 + r] = and_or(w8, 0x000F000Fu, one);
-    h[12 + r] = and_or(w8, 0x00F000F0u, one);
+    h[r] = and_or(w, 0x000F000Fu, c0);
+    h[4 + r] = and_or(w, 0x00F000F0u, c4);
+    h[8 + r] = and_or(w8, 0x000F000Fu, c0);
+    h[12 + r] = and_or(w8, 0x00F000F0u, c4);
   }
 }
 __host__ __device__ constexpr int slot_class_nib(int c) { return (c >> 2) & 1; }

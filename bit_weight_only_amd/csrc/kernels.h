@@ -10,6 +10,12 @@
 namespace lbq {
 
 hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, hipStream_t s);
+// Rotation into the folded slot order (u32 slot c of each 32-chunk holds
+// (x'[c], x'[c+16])), with the per-(group, token) sums sums[g * M + m] =
+// (P, T) the GEMM's code decode needs for code width `bits`; also zeroes
+// n_counters u32 at counters.
+hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, int bits, uint16_t *out,
+                                float2 *sums, uint32_t *counters, int n_counters, hipStream_t s);
 
 // RTN dequant-GEMV for 1 <= M <= 16 on already-rotated activations xr [M][K].
 hipError_t launch_gemv_rtn(const void *planes, const void *meta, const uint16_t *xr, uint16_t *y, int M, int K,
@@ -24,15 +30,25 @@ void gemv_fold_shape(int M, int K, int N, int &lanes, int &rb, int &grid_cap);
 hipError_t launch_gemv_fold(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs, uint16_t *y,
                             int M, int K, int N, int bits, int lanes, int rb, int grid_cap, hipStream_t s);
 
-// RTN dequant-GEMM on MFMA for any M >= 1 on rotated activations xr [M][K].
-hipError_t launch_gemm_rtn(const void *planes, const void *meta, const uint16_t *xr, uint16_t *y, int M, int K,
-                           int N, int bits, hipStream_t s);
-
 // Product-VQ GEMV (M <= 16) and MFMA GEMM on rotated activations.
 hipError_t launch_gemv_pvq(const uint8_t *idx, const uint16_t *scale, const uint8_t *codebook, const uint16_t *xr,
                            uint16_t *y, int M, int K, int N, hipStream_t s);
-hipError_t launch_gemm_pvq(const uint8_t *idx, const uint16_t *scale, const uint8_t *codebook, const uint16_t *xr,
-                           uint16_t *y, int M, int K, int N, hipStream_t s);
+// MFMA dequant-GEMM (RTN planes, format 0, or product-VQ, format 1) on
+// activations rotated into the folded slot order (launch_rotate_folded). The
+// plan fixes the tiling and the split-K count; split-K needs
+// gemm_scratch_bytes(plan) of scratch whose arrival counters
+// (gemm_counter_ptr, gemm_counters of them) are zero when the GEMM starts.
+struct GemmPlan {
+  int nb, mt, S, n_tiles, m_tiles;
+};
+GemmPlan gemm_plan(int M, int K, int N);
+size_t gemm_scratch_bytes(const GemmPlan &p);
+int gemm_counters(const GemmPlan &p);
+uint32_t *gemm_counter_ptr(const GemmPlan &p, void *scratch);
+hipError_t launch_gemm(const GemmPlan &p, int format, int bits, const void *planes, const void *meta,
+                       const uint8_t *codebook, const uint16_t *xf, const float2 *sums, uint16_t *y, int M, int K,
+                       int N, void *scratch, hipStream_t s);
+
 
 hipError_t launch_unpack_rtn(const void *planes, int K, int N, int bits, uint8_t *codes, hipStream_t s);
 

@@ -9,6 +9,8 @@
 #include "gemv_core.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace lbq {
 
 __global__ void __launch_bounds__(256) rotate_kernel(const uint32_t *__restrict__ x, const int8_t *__restrict__ signs,
@@ -28,6 +30,64 @@ __global__ void __launch_bounds__(256) rotate_kernel(const uint32_t *__restrict_
   const float c = kInvSqrt128;
   out[(base >> 1) + lane] = static_cast<uint32_t>(f32_to_f16_bits(v0 * c)) |
                             (static_cast<uint32_t>(f32_to_f16_bits(v1 * c)) << 16);
+}
+
+// Same rotation, written in the folded slot order the MFMA GEMM stages: in
+// each 32-element chunk, u32 slot c holds (x'[c], x'[c + 16]). Lane l and lane
+// l ^ 8 hold the two halves of the same slots and swap one value, so every lane
+// writes one whole slot. Per (group g, token m) it also writes the sums the
+// GEMM's decode needs, sums[g * M + m] = (P, T): P = sum_k 2^(10 - m_k) x'_k
+// over the slot classes m_k of the weight's code width, T = sum_k x'_k, both
+// of the fp16-rounded x'. And it clears n_counters u32 counters (the GEMM's
+// split-K arrival counters) before the GEMM launch that uses them.
+template <int BITS>
+__global__ void __launch_bounds__(256) rotate_folded_kernel(const uint32_t *__restrict__ x,
+                                                            const int8_t *__restrict__ signs,
+                                                            uint32_t *__restrict__ out, float2 *__restrict__ sums,
+                                                            int M, int K, uint32_t *__restrict__ counters,
+                                                            int n_counters) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_counters; i += gridDim.x * 256) counters[i] = 0;
+  const int lane = threadIdx.x & 63;
+  const int blocks_per_row = K / kGroup;
+  const long blk = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (blk >= static_cast<long>(M) * blocks_per_row) return;
+  const int m = static_cast<int>(blk / blocks_per_row);
+  const int b = static_cast<int>(blk % blocks_per_row);
+  const long base = static_cast<long>(m) * K + b * kGroup;
+  const uint32_t xv = x[(base >> 1) + lane];
+  const int k0 = b * kGroup + 2 * lane;
+  float v0 = half_lo(xv) * static_cast<float>(signs[k0]);
+  float v1 = half_hi(xv) * static_cast<float>(signs[k0 + 1]);
+  fwht128_wave(v0, v1, lane);
+  const uint32_t r0 = f32_to_f16_bits(v0 * kInvSqrt128), r1 = f32_to_f16_bits(v1 * kInvSqrt128);
+  // element 2l (+1) is slot (2l & 15) (+1) of chunk l >> 4, half (l >> 3) & 1
+  const bool hi = (lane >> 3) & 1;
+  const uint32_t give = hi ? r0 : r1;
+  const uint32_t got = static_cast<uint32_t>(__shfl_xor(static_cast<int>(give), 8));
+  const uint32_t word = hi ? (got | (r1 << 16)) : (r0 | (got << 16));
+  const int slot = ((2 * lane) & 15) + (hi ? 1 : 0);
+  out[(base >> 1) + (lane >> 4) * 16 + slot] = word;
+  // slots 2l & 15 and its successor share one class
+  const float pair = f16_bits_to_f32(r0) + f16_bits_to_f32(r1);
+  float P = slot_weight<BITS>((2 * lane) & 15) * pair, T = pair;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    P += __shfl_xor(P, off);
+    T += __shfl_xor(T, off);
+  }
+  if (lane == 0) sums[static_cast<long>(b) * M + m] = make_float2(P, T);
+}
+
+hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, int bits, uint16_t *out,
+                                float2 *sums, uint32_t *counters, int n_counters, hipStream_t s) {
+  const long nblk = static_cast<long>(M) * (K / kGroup);
+  const long need = std::max<long>((nblk + 3) / 4, (n_counters + 255) / 256);
+  if (need == 0) return hipSuccess;
+  auto kern = bits == 2 ? rotate_folded_kernel<2> : rotate_folded_kernel<4>;   // 3 and 4 bits share classes
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(need)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t *>(x), signs, reinterpret_cast<uint32_t *>(out), sums, M, K,
+                     counters, n_counters);
+  return hipGetLastError();
 }
 
 hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, hipStream_t s) {

@@ -79,8 +79,8 @@ typedef enum {
   LBQ_FMT_PVQ_4x8 = 1
 } lbq_format;
 
-/* Kernel path for lbq_linear_forward_path. AUTO picks GEMV for M <= 16 and the
- * MFMA GEMM above; forcing GEMV needs M <= 16. */
+/* Kernel path for lbq_linear_forward_path. AUTO picks the GEMV for M <= 3 and
+ * the MFMA GEMM above (measured crossover); forcing the GEMV needs M <= 16. */
 typedef enum {
   LBQ_PATH_AUTO = 0,
   LBQ_PATH_GEMV = 1,
@@ -145,8 +145,8 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
 /* y[M][N] (fp16) = x[M][K] (fp16) W_hat^T, W_hat the weight w decodes to.
  * The activation rotation runs either inside the GEMV's prologue (one or two
  * tokens on rows of up to 8192 / 4096 inputs, signs 16-byte aligned) or as its
- * own launch into the workspace, followed by the dequant-GEMV (M <= 16) or the
- * MFMA dequant-GEMM (M >= 17). Accumulation is fp32. */
+ * own launch into the workspace, followed by the dequant-GEMV (M <= 3) or the
+ * MFMA dequant-GEMM (M >= 4). Accumulation is fp32. */
 lbq_status lbq_linear_forward(const lbq_weight *w, const uint16_t *x, int32_t M,
                               uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 
