@@ -15,8 +15,10 @@ The steps are replayed from a HIP graph captured once (no Python launch
 overhead in the timed region), inputs resident in HBM. The dominant kernel is
 the single-token GEMV with the fused rotation (gemv_fold_kernel; it serves the
 three K = 4096 linears); its launch durations are measured live with HIP
-events recorded on the stream it is launched on, around each of its launches
-in an eager pass over the same steps; roofline.achieved = its algorithmic
+events on the stream it is launched on, for each of its launches
+in an eager pass over the same steps (lbq_linear_forward_timed: the kernel's
+launch itself carries the events, so they hold its own begin / end times, the
+same quantity rocprofv3 reports); roofline.achieved = its algorithmic
 bytes (packed planes + scale/zero words) summed over those launches / their
 summed durations. roofline.traffic (HBM bytes per launch, from rocprofv3
 FETCH_SIZE + WRITE_SIZE scaled by a copy kernel of known size) is read from
@@ -172,14 +174,18 @@ class Stack:
 
 
 def event_pass(torch, stack, reps=2):
-    """Eager steps on one stream with HIP events recorded on that stream around
-    every lbq_linear_forward (a sleep kernel first lets the host run ahead so
-    the GPU executes the launches back to back). {shape: [seconds]}."""
+    """Eager steps on one stream through lbq_linear_forward_timed: HIP events
+    created on this process's runtime take the main kernel's own begin / end
+    times (for the single-token GEMV, the kernel launch itself carries them).
+    {shape: [seconds]}."""
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
-    fwd = stack.lib.lbq_linear_forward
+    fwd = stack.lib.lbq_linear_forward_timed
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(len(stack.order) * reps)]
+    for e0, e1 in pairs:          # create the underlying events
+        e0.record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     torch.cuda._sleep(300_000_000)
     done = []
@@ -188,9 +194,8 @@ def event_pass(torch, stack, reps=2):
         for sh, (w, x, M, y, ws, n) in stack.order:
             e0, e1 = pairs[i]
             i += 1
-            e0.record(stream)
-            check(fwd(w, x, M, y, ws, n, sp), "lbq_linear_forward")
-            e1.record(stream)
+            check(fwd(w, x, M, y, ws, n, sp, ctypes.c_void_p(e0.cuda_event), ctypes.c_void_p(e1.cuda_event)),
+                  "lbq_linear_forward_timed")
             done.append((sh["name"], e0, e1))
     torch.cuda.synchronize()
     per = {}
@@ -200,8 +205,9 @@ def event_pass(torch, stack, reps=2):
 
 
 def calibration_copy(torch):
-    """A plain elementwise copy of CALIB_BYTES (read and write): the reference
-    dispatch the counter summary scales FETCH_SIZE / WRITE_SIZE by."""
+    """A plain elementwise copy of CALIB_BYTES (read and write; torch's unary
+    multiply-by-one kernel): the reference dispatch the counter summary scales
+    FETCH_SIZE / WRITE_SIZE by."""
     n = CALIB_BYTES // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda:0")
     b = torch.empty_like(a)
@@ -438,8 +444,8 @@ def summarize(fetch_dir, write_dir, trace_dir, command, out_path):
 
     k_fetch, n1 = pick(fetch, DOMINANT)
     k_write, n2 = pick(write, DOMINANT)
-    c_fetch, n3 = pick(fetch, "elementwise")
-    c_write, n4 = pick(write, "elementwise")
+    c_fetch, n3 = pick(fetch, "AUnaryFunctor")   # the multiply-by-one copy of calibration_copy()
+    c_write, n4 = pick(write, "AUnaryFunctor")
     f_fetch = CALIB_BYTES / (c_fetch * 1024.0)
     f_write = CALIB_BYTES / (c_write * 1024.0)
     traffic = k_fetch * 1024.0 * f_fetch + k_write * 1024.0 * f_write

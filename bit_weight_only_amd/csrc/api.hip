@@ -40,6 +40,53 @@ size_t linear_ws_bytes(int M, int K, int N) {
          gemm_scratch_bytes(gemm_plan(M, K, N));
 }
 
+lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint16_t *y, void *ws, size_t ws_bytes,
+                        int32_t path, void *stream, hipEvent_t ev0, hipEvent_t ev1) {
+  lbq_status st = check_weight(w);
+  if (st != LBQ_OK) return st;
+  if (M < 0) return LBQ_ERR_SHAPE;
+  if (path < LBQ_PATH_AUTO || path > LBQ_PATH_GEMM) return LBQ_ERR_SHAPE;
+  if (path == LBQ_PATH_GEMV && M > 16) return LBQ_ERR_SHAPE;
+  if (M == 0) return LBQ_OK;
+  if (!x || !y || !ws) return LBQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return LBQ_ERR_ALIGN;
+  if (ws_bytes < linear_ws_bytes(M, w->K, w->N)) return LBQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the MFMA GEMM's decode costs the same at 4 tokens as at 16; below that the
+  // VALU GEMV is faster
+  const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 3);
+  // One or two tokens on short rows: rotation fused into the decoder, one launch.
+  if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_fold_supported(M, w->K) && aligned16(w->signs))
+    return hip_status(launch_gemv_fold(w->planes, w->meta, x, w->signs, y, M, w->K, w->N, w->bits, 0, 0, 0, s, ev0,
+                                       ev1));
+  uint16_t *xr = static_cast<uint16_t *>(ws);
+  if (!gemv) {
+    // MFMA GEMM: rotation into the folded order (clearing the split-K counters), then the GEMM
+    const GemmPlan gp = gemm_plan(M, w->K, w->N);
+    float2 *sums =
+        reinterpret_cast<float2 *>(static_cast<uint8_t *>(ws) + round_up(static_cast<size_t>(M) * w->K * 2, kAlign));
+    void *scratch = reinterpret_cast<uint8_t *>(sums) + round_up(static_cast<size_t>(M) * (w->K / 128) * 8, kAlign);
+    if (launch_rotate_folded(x, M, w->K, w->signs, w->bits, xr, sums, gemm_counter_ptr(gp, scratch),
+                             gemm_counters(gp), s) != hipSuccess)
+      return LBQ_ERR_HIP;
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return LBQ_ERR_HIP;
+    if (launch_gemm(gp, w->format, w->bits, w->planes, w->meta, static_cast<const uint8_t *>(w->codebook), xr, sums, y,
+                    M, w->K, w->N, scratch, s) != hipSuccess)
+      return LBQ_ERR_HIP;
+    return (ev1 && hipEventRecord(ev1, s) != hipSuccess) ? LBQ_ERR_HIP : LBQ_OK;
+  }
+  hipError_t e = launch_rotate(x, M, w->K, w->signs, xr, s);
+  if (e != hipSuccess) return LBQ_ERR_HIP;
+  if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return LBQ_ERR_HIP;
+  if (w->format == LBQ_FMT_RTN_PLANES)
+    e = launch_gemv_rtn(w->planes, w->meta, xr, y, M, w->K, w->N, w->bits, s);
+  else
+    e = launch_gemv_pvq(static_cast<const uint8_t *>(w->planes), static_cast<const uint16_t *>(w->meta),
+                        static_cast<const uint8_t *>(w->codebook), xr, y, M, w->K, w->N, s);
+  if (e != hipSuccess) return LBQ_ERR_HIP;
+  return (ev1 && hipEventRecord(ev1, s) != hipSuccess) ? LBQ_ERR_HIP : LBQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,41 +152,13 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes) {
 
 lbq_status lbq_linear_forward_path(const lbq_weight *w, const uint16_t *x, int32_t M, uint16_t *y, void *ws,
                                    size_t ws_bytes, int32_t path, void *stream) {
-  lbq_status st = check_weight(w);
-  if (st != LBQ_OK) return st;
-  if (M < 0) return LBQ_ERR_SHAPE;
-  if (path < LBQ_PATH_AUTO || path > LBQ_PATH_GEMM) return LBQ_ERR_SHAPE;
-  if (path == LBQ_PATH_GEMV && M > 16) return LBQ_ERR_SHAPE;
-  if (M == 0) return LBQ_OK;
-  if (!x || !y || !ws) return LBQ_ERR_NULL;
-  if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return LBQ_ERR_ALIGN;
-  if (ws_bytes < linear_ws_bytes(M, w->K, w->N)) return LBQ_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // the MFMA GEMM's decode costs the same at 4 tokens as at 16; below that the
-  // VALU GEMV is faster
-  const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 3);
-  // One or two tokens on short rows: rotation fused into the decoder, one launch.
-  if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_fold_supported(M, w->K) && aligned16(w->signs))
-    return hip_status(launch_gemv_fold(w->planes, w->meta, x, w->signs, y, M, w->K, w->N, w->bits, 0, 0, 0, s));
-  uint16_t *xr = static_cast<uint16_t *>(ws);
-  if (!gemv) {
-    // MFMA GEMM: rotation into the folded order (clearing the split-K counters), then the GEMM
-    const GemmPlan gp = gemm_plan(M, w->K, w->N);
-    float2 *sums =
-        reinterpret_cast<float2 *>(static_cast<uint8_t *>(ws) + round_up(static_cast<size_t>(M) * w->K * 2, kAlign));
-    void *scratch = reinterpret_cast<uint8_t *>(sums) + round_up(static_cast<size_t>(M) * (w->K / 128) * 8, kAlign);
-    if (launch_rotate_folded(x, M, w->K, w->signs, w->bits, xr, sums, gemm_counter_ptr(gp, scratch),
-                             gemm_counters(gp), s) != hipSuccess)
-      return LBQ_ERR_HIP;
-    return hip_status(launch_gemm(gp, w->format, w->bits, w->planes, w->meta,
-                                  static_cast<const uint8_t *>(w->codebook), xr, sums, y, M, w->K, w->N, scratch, s));
-  }
-  hipError_t e = launch_rotate(x, M, w->K, w->signs, xr, s);
-  if (e != hipSuccess) return LBQ_ERR_HIP;
-  if (w->format == LBQ_FMT_RTN_PLANES)
-    return hip_status(launch_gemv_rtn(w->planes, w->meta, xr, y, M, w->K, w->N, w->bits, s));
-  return hip_status(launch_gemv_pvq(static_cast<const uint8_t *>(w->planes), static_cast<const uint16_t *>(w->meta),
-                                    static_cast<const uint8_t *>(w->codebook), xr, y, M, w->K, w->N, s));
+  return forward_impl(w, x, M, y, ws, ws_bytes, path, stream, nullptr, nullptr);
+}
+
+lbq_status lbq_linear_forward_timed(const lbq_weight *w, const uint16_t *x, int32_t M, uint16_t *y, void *ws,
+                                    size_t ws_bytes, void *stream, void *start_event, void *stop_event) {
+  return forward_impl(w, x, M, y, ws, ws_bytes, LBQ_PATH_AUTO, stream, static_cast<hipEvent_t>(start_event),
+                      static_cast<hipEvent_t>(stop_event));
 }
 
 lbq_status lbq_linear_forward(const lbq_weight *w, const uint16_t *x, int32_t M, uint16_t *y, void *ws,

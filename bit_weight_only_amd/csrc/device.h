@@ -172,6 +172,33 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
 }
 
+// Value of lane (l ^ X) for lane l, in registers (no LDS crossbar): DPP for
+// X = 1, 2, 4 (half-row mirror then quad reversal), 8 (row rotate by 8);
+// v_permlane16_swap / v_permlane32_swap of the value with itself for 16 / 32
+// (each returns the two 16-lane (32-lane) halves exchanged in one of its two
+// results; the lane picks the one holding its partner).
+template <int X>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v) {
+  const int i = static_cast<int>(v);
+  if constexpr (X == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (X == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (X == 4) {
+    const int m = __builtin_amdgcn_update_dpp(0, i, 0x141, 0xF, 0xF, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false));
+  } else if constexpr (X == 8) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, i, 0x128, 0xF, 0xF, false));
+  } else if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    static_assert(X == 32, "xor distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+
 // fp8 e4m3 (OCP "fn": bias 7, no infinities, S.1111.111 = NaN) to fp16 bits.
 // Every finite e4m3 value is exact in fp16.
 __device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t b) {

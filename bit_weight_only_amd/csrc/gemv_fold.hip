@@ -26,6 +26,8 @@
 #include "gemv_core.h"
 #include "kernels.h"
 
+#include <hip/hip_ext.h>
+
 namespace lbq {
 
 namespace {
@@ -283,7 +285,7 @@ __global__ void __launch_bounds__(256) gemv_fold_kernel(const uint4 *__restrict_
 
 template <int BITS, int MT, int L, int RB>
 hipError_t launch_fold(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs, uint16_t *y,
-                       int M, int K, int N, int grid_cap, hipStream_t s) {
+                       int M, int K, int N, int grid_cap, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const int G = K / kGroup;
   const size_t lds = static_cast<size_t>(MT) * G * (256 + 16);
   auto kern = gemv_fold_kernel<BITS, MT, L, RB>;
@@ -295,17 +297,24 @@ hipError_t launch_fold(const void *planes, const void *meta, const uint16_t *x, 
   constexpr int ROWS = (256 / L) * RB;
   const int tiles = (N + ROWS - 1) / ROWS;
   const unsigned grid = static_cast<unsigned>(min(tiles, grid_cap));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, reinterpret_cast<const uint4 *>(planes),
-                     reinterpret_cast<const uint32_t *>(meta), reinterpret_cast<const uint4 *>(x),
-                     reinterpret_cast<const uint4 *>(signs), y, M, K, N);
+  const uint4 *pl = reinterpret_cast<const uint4 *>(planes);
+  const uint32_t *mt = reinterpret_cast<const uint32_t *>(meta);
+  const uint4 *xv = reinterpret_cast<const uint4 *>(x);
+  const uint4 *sv = reinterpret_cast<const uint4 *>(signs);
+  if (start || stop)   // the events take this kernel's own begin / end times
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(256), static_cast<uint32_t>(lds), s, start, stop, 0, pl, mt, xv, sv, y,
+                          M, K, N);
+  else
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, pl, mt, xv, sv, y, M, K, N);
   return hipGetLastError();
 }
 
 template <int BITS, int MT>
 hipError_t launch_mt(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs, uint16_t *y, int M,
-                     int K, int N, int lanes, int rb, int grid_cap, hipStream_t s) {
-#define LBQ_FOLD(LL, R) \
-  if (lanes == LL && rb == R) return launch_fold<BITS, MT, LL, R>(planes, meta, x, signs, y, M, K, N, grid_cap, s);
+                     int K, int N, int lanes, int rb, int grid_cap, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+#define LBQ_FOLD(LL, R)                                                                                   \
+  if (lanes == LL && rb == R)                                                                             \
+    return launch_fold<BITS, MT, LL, R>(planes, meta, x, signs, y, M, K, N, grid_cap, s, start, stop);
   LBQ_FOLD(16, 1) LBQ_FOLD(32, 1) LBQ_FOLD(64, 1) LBQ_FOLD(32, 2)
 #undef LBQ_FOLD
   return hipErrorInvalidValue;
@@ -330,12 +339,13 @@ bool gemv_fold_supported(int M, int K) {
 }
 
 hipError_t launch_gemv_fold(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs, uint16_t *y,
-                            int M, int K, int N, int bits, int lanes, int rb, int grid_cap, hipStream_t s) {
+                            int M, int K, int N, int bits, int lanes, int rb, int grid_cap, hipStream_t s,
+                            hipEvent_t start, hipEvent_t stop) {
   if (M < 1 || M > 2 || (reinterpret_cast<uintptr_t>(signs) & 15u) != 0) return hipErrorInvalidValue;
   if (lanes <= 0) gemv_fold_shape(M, K, N, lanes, rb, grid_cap);
 #define LBQ_MT(B)                                                                                  \
-  return M == 1 ? launch_mt<B, 1>(planes, meta, x, signs, y, M, K, N, lanes, rb, grid_cap, s)       \
-                : launch_mt<B, 2>(planes, meta, x, signs, y, M, K, N, lanes, rb, grid_cap, s);
+  return M == 1 ? launch_mt<B, 1>(planes, meta, x, signs, y, M, K, N, lanes, rb, grid_cap, s, start, stop) \
+                : launch_mt<B, 2>(planes, meta, x, signs, y, M, K, N, lanes, rb, grid_cap, s, start, stop);
   switch (bits) {
     case 2: LBQ_MT(2)
     case 3: LBQ_MT(3)

@@ -24,11 +24,13 @@ hipError_t launch_gemv_rtn(const void *planes, const void *meta, const uint16_t 
 // RTN dequant-GEMV on raw activations x [M][K] (M = 1 or 2) with the rotation
 // in the kernel's prologue: one launch, no workspace. signs must be 16-byte
 // aligned. gemv_fold_supported says where this path is the faster one;
-// lanes <= 0 picks the launch shape (gemv_fold_shape).
+// lanes <= 0 picks the launch shape (gemv_fold_shape). Non-null events take
+// the kernel's own begin / end times (hipExtLaunchKernel).
 bool gemv_fold_supported(int M, int K);
 void gemv_fold_shape(int M, int K, int N, int &lanes, int &rb, int &grid_cap);
 hipError_t launch_gemv_fold(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs, uint16_t *y,
-                            int M, int K, int N, int bits, int lanes, int rb, int grid_cap, hipStream_t s);
+                            int M, int K, int N, int bits, int lanes, int rb, int grid_cap, hipStream_t s,
+                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // Product-VQ GEMV (M <= 16) and MFMA GEMM on rotated activations.
 hipError_t launch_gemv_pvq(const uint8_t *idx, const uint16_t *scale, const uint8_t *codebook, const uint16_t *xr,

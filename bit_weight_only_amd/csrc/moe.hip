@@ -3,9 +3,10 @@
 // in a Hadamard-rotated basis: LLaDA2.2-mini Orin Nano card, "Routed Experts").
 //
 // Passes, all on the caller's stream:
-//   1. route:   one workgroup; per token the top_k logits (ties to the lower
-//               expert id) and softmax weights over them; per-expert counts,
-//               exclusive offsets, and the assignment list grouped by expert.
+//   1. route:   one workgroup; per token (a wavefront each) the top_k logits
+//               (ties to the lower expert id) and softmax weights over them;
+//               per-expert counts, exclusive offsets, and the assignment list
+//               grouped by expert.
 //   2. rotate:  x' = R_hidden x once per token (the rotate kernel).
 //   3. gate|up: one workgroup per (expert, 128-wide block of the ffn axis);
 //               inactive experts exit at once. It decodes the 128 gate rows and
@@ -25,17 +26,35 @@ namespace lbq {
 
 namespace {
 
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxAssignments = 8192;
 constexpr int kMaxTokChunk = 8;
 
 // ------------------------------------------------------------------ router
 
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+// Order-preserving map of a float to u32 (larger float -> larger u32) and back.
+__device__ __forceinline__ uint32_t float_order(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float float_unorder(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+template <int X>
+__device__ __forceinline__ uint64_t max_with_xor_u64(uint64_t v) {
+  const uint32_t lo = xor_lane_u32<X>(static_cast<uint32_t>(v));
+  const uint32_t hi = xor_lane_u32<X>(static_cast<uint32_t>(v >> 32));
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > v ? o : v;
+}
+template <int X>
+__device__ __forceinline__ float add_xor(float v) {
+  return v + __uint_as_float(xor_lane_u32<X>(__float_as_uint(v)));
 }
 
+// PER: experts per lane (E <= 64 PER).
+template <int PER>
 __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *__restrict__ logits, int M, int E,
                                                                   int top_k, int32_t *__restrict__ ids,
                                                                   float *__restrict__ weights,
@@ -47,51 +66,52 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
   __shared__ int32_t s_cur[kMaxExperts];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kWaves = kRouteThreads / 64;
-  constexpr int kPerLane = kMaxExperts / 64;
 
-  // 1. top-k per token, one wavefront per token.
+  // 1. top-k per token, one wavefront per token. Expert e = lane + 64 i is the
+  //    key (order(logit) << 32 | kMaxExperts - 1 - e): the largest key is the
+  //    largest logit, ties to the lower id; a selected key is cleared to 0.
   for (int t = wave; t < M; t += kWaves) {
-    float v[kPerLane];
-    uint32_t taken = 0;
+    // all loads first, unconditionally at clamped indices, then the keys
+    float lv[PER];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
+    for (int i = 0; i < PER; ++i) lv[i] = logits[static_cast<size_t>(t) * E + min(lane + 64 * i, E - 1)];
+    uint64_t key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
       const int e = lane + 64 * i;
-      v[i] = (e < E) ? logits[static_cast<size_t>(t) * E + e] : 0.f;
+      key[i] = e < E ? (static_cast<uint64_t>(float_order(lv[i])) << 32) | static_cast<uint32_t>(kMaxExperts - 1 - e)
+                     : 0;
     }
-    float sel0 = 0.f, denom = 0.f;
-    float selv[32];
+    // lane r keeps the r-th selected logit (selection order is descending)
+    float sel0 = 0.f, mine = 0.f;
     for (int r = 0; r < top_k; ++r) {
-      float bv = 0.f;
-      int bi = 0x7FFFFFFF;
+      uint64_t best = 0;
 #pragma unroll
-      for (int i = 0; i < kPerLane; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u) && (bi == 0x7FFFFFFF || better(v[i], e, bv, bi))) {
-          bv = v[i];
-          bi = e;
-        }
-      }
+      for (int i = 0; i < PER; ++i) best = key[i] > best ? key[i] : best;
+      best = max_with_xor_u64<32>(best);
+      best = max_with_xor_u64<16>(best);
+      best = max_with_xor_u64<8>(best);
+      best = max_with_xor_u64<4>(best);
+      best = max_with_xor_u64<2>(best);
+      best = max_with_xor_u64<1>(best);
+      const int e = kMaxExperts - 1 - static_cast<int>(static_cast<uint32_t>(best));
+      const float v = float_unorder(static_cast<uint32_t>(best >> 32));
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (r == 0) sel0 = bv;
-      selv[r] = bv;
-      if (lane == 0) s_ids[t * top_k + r] = bi;
+      for (int i = 0; i < PER; ++i)
+        if (i == (e >> 6) && lane == (e & 63)) key[i] = 0;
+      if (r == 0) sel0 = v;
+      if (lane == r) mine = v;
+      if (lane == 0) s_ids[t * top_k + r] = e;
     }
-    for (int r = 0; r < top_k; ++r) denom += __expf(selv[r] - sel0);
-    if (lane < top_k) {
-      float mine = 0.f;
-      for (int r = 0; r < top_k; ++r)
-        if (r == lane) mine = selv[r];
-      weights[t * top_k + lane] = __expf(mine - sel0) / denom;
-    }
+    // softmax over the selected logits (shifted by the largest)
+    const float ex = lane < top_k ? __expf(mine - sel0) : 0.f;
+    float denom = add_xor<32>(ex);
+    denom = add_xor<16>(denom);
+    denom = add_xor<8>(denom);
+    denom = add_xor<4>(denom);
+    denom = add_xor<2>(denom);
+    denom = add_xor<1>(denom);
+    if (lane < top_k) weights[t * top_k + lane] = ex / denom;
   }
   for (int e = threadIdx.x; e < E; e += kRouteThreads) s_cnt[e] = 0;
   __syncthreads();
@@ -101,38 +121,64 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
     atomicAdd(&s_cnt[s_ids[a]], 1);
   }
   __syncthreads();
-  // 2. exclusive offsets
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = run;
-      s_cur[e] = run;
-      counts[e] = s_cnt[e];
-      run += s_cnt[e];
+  // 2. exclusive offsets: thread i owns experts kPerThread i .. kPerThread (i + 1) - 1;
+  //    scan of the per-thread totals within each wave, then across the waves
+  {
+    constexpr int kPerThread = (kMaxExperts + kRouteThreads - 1) / kRouteThreads;
+    __shared__ int32_t s_wave[kWaves];
+    int own[kPerThread];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int e = threadIdx.x * kPerThread + j;
+      own[j] = e < E ? s_cnt[e] : 0;
+      sum += own[j];
     }
-    offsets[E] = run;
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_wave[w];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int e = threadIdx.x * kPerThread + j;
+      if (e < E) {
+        offsets[e] = run;
+        s_cur[e] = run;
+        counts[e] = own[j];
+      }
+      run += own[j];
+    }
+    if (threadIdx.x == kRouteThreads - 1) offsets[E] = run;
   }
   __syncthreads();
-  // 3. assignment list grouped by expert, increasing assignment index within an expert
-  for (int c0 = 0; c0 < MK; c0 += kRouteThreads) {
-    const int a = c0 + threadIdx.x;
-    const int n_in = min(kRouteThreads, MK - c0);
-    const int e = (a < MK) ? s_ids[a] : -1;
-    int rank = 0;
-    bool last = true;
-    if (a < MK) {
-      for (int i = 0; i < n_in; ++i) {
-        const int ei = s_ids[c0 + i];
-        if (ei == e) {
-          if (i < static_cast<int>(threadIdx.x)) ++rank;
-          else if (i > static_cast<int>(threadIdx.x)) last = false;
-        }
+  // 3. assignment list grouped by expert, increasing assignment index within an
+  //    expert: wavefront 0 walks the assignments in chunks of 64; lane l's rank
+  //    among the chunk's earlier lanes with the same expert comes from a scan
+  //    of the chunk's expert ids, and the expert's last lane in the chunk moves
+  //    its write position past the chunk's entries.
+  if (wave == 0) {
+    for (int c0 = 0; c0 < MK; c0 += 64) {
+      const int a = c0 + lane;
+      const int e = a < MK ? s_ids[a] : -1;
+      const int n = __builtin_amdgcn_readfirstlane(min(64, MK - c0));
+      int rank = 0, cnt = 0;
+      for (int jj = 0; jj < n; ++jj) {
+        const int same = __builtin_amdgcn_readlane(e, jj) == e;
+        rank += (jj < lane) & same;
+        cnt += same;
       }
-      perm[s_cur[e] + rank] = a;
+      if (a < MK) {
+        const int base = s_cur[e];
+        perm[base + rank] = a;
+        if (rank == cnt - 1) s_cur[e] = base + cnt;
+      }
     }
-    __syncthreads();
-    if (a < MK && last) s_cur[e] += rank + 1;
-    __syncthreads();
   }
 }
 
@@ -300,8 +346,10 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const float *__restric
 
 hipError_t launch_moe_route(const float *logits, int M, int E, int top_k, int32_t *ids, float *weights,
                             int32_t *counts, int32_t *offsets, int32_t *perm, hipStream_t s) {
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, logits, M, E, top_k, ids, weights, counts,
-                     offsets, perm);
+  auto kern = E <= 64 ? moe_route_kernel<1> : E <= 256 ? moe_route_kernel<4> : E <= 512 ? moe_route_kernel<8>
+                                                                                  : moe_route_kernel<16>;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kRouteThreads), 0, s, logits, M, E, top_k, ids, weights, counts, offsets,
+                     perm);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ STATUS = {
 # Every symbol include/lbq.h declares.
 EXPORTS = [
     "lbq_status_string", "lbq_packed_bytes", "lbq_pack", "lbq_linear_workspace", "lbq_linear_forward",
-    "lbq_linear_forward_path", "lbq_moe_workspace", "lbq_moe_forward", "lbq_moe_route", "lbq_unpack_codes",
+    "lbq_linear_forward_path", "lbq_linear_forward_timed", "lbq_moe_workspace", "lbq_moe_forward", "lbq_moe_route", "lbq_unpack_codes",
     "lbq_rotate",
 ]
 
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.lbq_linear_workspace.argtypes = [ctypes.POINTER(Weight), c_i32, p_sz]
         L.lbq_linear_forward.argtypes = [ctypes.POINTER(Weight), c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]
         L.lbq_linear_forward_path.argtypes = [ctypes.POINTER(Weight), c_vp, c_i32, c_vp, c_vp, c_sz, c_i32, c_vp]
+        L.lbq_linear_forward_timed.argtypes = [ctypes.POINTER(Weight), c_vp, c_i32, c_vp, c_vp, c_sz, c_vp, c_vp, c_vp]
         L.lbq_moe_workspace.argtypes = [ctypes.POINTER(Moe), c_i32, p_sz]
         L.lbq_moe_forward.argtypes = [ctypes.POINTER(Moe), c_vp, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]
         L.lbq_moe_route.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]

@@ -155,6 +155,17 @@ lbq_status lbq_linear_forward_path(const lbq_weight *w, const uint16_t *x, int32
                                    uint16_t *y, void *ws, size_t ws_bytes, int32_t path,
                                    void *stream);
 
+/* lbq_linear_forward (AUTO path) with the main kernel's duration bracketed by
+ * two caller-owned HIP events (hipEvent_t created with timing enabled; either
+ * may be NULL). For the single-token GEMV with the rotation in its prologue
+ * the events take that kernel's own begin and end times (hipExtLaunchKernel);
+ * on the other paths they are recorded on the stream right before and after
+ * the GEMV / GEMM launch (after the separate rotation launch). For measuring
+ * the kernel; the result is the one lbq_linear_forward gives. */
+lbq_status lbq_linear_forward_timed(const lbq_weight *w, const uint16_t *x, int32_t M,
+                                    uint16_t *y, void *ws, size_t ws_bytes, void *stream,
+                                    void *start_event, void *stop_event);
+
 /* Workspace bytes lbq_moe_forward needs for M tokens (host query). */
 lbq_status lbq_moe_workspace(const lbq_moe *m, int32_t M, size_t *bytes);
 
