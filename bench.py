@@ -13,9 +13,9 @@ weights from HBM.
 
 The steps are replayed from a HIP graph captured once (no Python launch
 overhead in the timed region), inputs resident in HBM. The dominant kernel is
-the single-token GEMV with the fused rotation (gemv_fold_kernel; it serves the
-three K = 4096 linears); its launch durations are measured live with HIP
-events on the stream it is launched on, for each of its launches
+the matrix-core GEMV with the fused rotation (gemv_mfma_kernel; it serves all
+four linears, one launch each); its launch durations are measured live with
+HIP events on the stream it is launched on, for each of its launches
 in an eager pass over the same steps (lbq_linear_forward_timed: the kernel's
 launch itself carries the events, so they hold its own begin / end times, the
 same quantity rocprofv3 reports); roofline.achieved = its algorithmic
@@ -55,11 +55,10 @@ import synth  # noqa: E402
 METRIC = "packed-weight HBM GB/s (% of peak) for 2-bit dequant-GEMV at M=1; TFLOP/s at M=64"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
-DOMINANT = "gemv_fold_kernel"
+DOMINANT = "gemv_mfma_kernel"
 # sources the dominant kernel is built from (traffic from counters is stale once they change)
-DOMINANT_SOURCES = ["bit_weight_only_amd/csrc/gemv_fold.hip", "bit_weight_only_amd/csrc/gemv_core.h",
-                    "bit_weight_only_amd/csrc/device.h"]
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "gemv_fold_dense_stack_m1.txt")
+DOMINANT_SOURCES = ["bit_weight_only_amd/csrc/gemv_mfma.hip", "bit_weight_only_amd/csrc/device.h"]
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "gemv_mfma_dense_stack_m1.txt")
 CALIB_BYTES = 512 << 20        # the copy kernel reads and writes this many bytes
 
 
@@ -452,11 +451,21 @@ def summarize(fetch_dir, write_dir, trace_dir, command, out_path):
     stats = []
     for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
         stats += list(csv.DictReader(open(f)))
+    trace = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        trace += list(csv.DictReader(open(f)))
+    # the event pass starts behind the one spin kernel (torch.cuda._sleep) of the command
+    spin = [int(r["Start_Timestamp"]) for r in trace if "spin_kernel" in r["Kernel_Name"]]
+    t_spin = max(spin) if spin else 0
+    dom = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+           if DOMINANT in r["Kernel_Name"] and int(r["Start_Timestamp"]) > t_spin]
+    dom_all = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace if DOMINANT in r["Kernel_Name"]]
     # the dominant kernel's launches in the stack: its algorithmic bytes per launch on average
-    stack_bytes = [planes_meta_bytes(k, n, 2) for (_, k, n) in synth.DENSE_STACK_SHAPES if k == 4096]
+    stack_bytes = [planes_meta_bytes(k, n, 2) for (_, k, n) in synth.DENSE_STACK_SHAPES]
     lines = [
-        "rocprofv3 summary: single-token dequant-GEMV with fused rotation (gemv_fold_kernel),",
-        "dense decode stack at M=1 (qkv 4096->6144, o 4096->4096, gate|up 4096->28672; 2-bit group-128).",
+        "rocprofv3 summary: matrix-core dequant-GEMV with fused rotation (gemv_mfma_kernel),",
+        "dense decode stack at M=1 (qkv 4096->6144, o 4096->4096, gate|up 4096->28672, down 14336->4096;",
+        "2-bit group-128).",
         "",
         f"commands (run from the repository root, cd /tmp && export TMPDIR=/tmp first):",
         f"  rocprofv3 --kernel-trace --stats -d <dir> -o k --output-format csv -- {command}",
@@ -472,17 +481,50 @@ def summarize(fetch_dir, write_dir, trace_dir, command, out_path):
                      f"{float(r['TotalDurationNs']) / 1e3:12.1f}")
     lines += [
         "",
+        f"{DOMINANT} launch durations from the trace: all {len(dom_all)} launches (graph replays and the",
+        f"event pass) {float(np.mean(dom_all)) if dom_all else float('nan'):.3f} us on average; the {len(dom)} "
+        f"launches of the event pass (after the spin",
+        f"kernel; the launches bench.py times with HIP events) {float(np.mean(dom)) if dom else float('nan'):.3f} us "
+        f"on average.",
+        "",
         f"counters (KiB per dispatch, mean): {DOMINANT}: FETCH_SIZE {k_fetch:.1f} (n={n1}), "
         f"WRITE_SIZE {k_write:.1f} (n={n2})",
         f"copy of {CALIB_BYTES} bytes (read and write): FETCH_SIZE {c_fetch:.1f} (n={n3}), WRITE_SIZE {c_write:.1f} "
         f"(n={n4})",
         f"scale factors (bytes per counter KiB / 1024): fetch {f_fetch:.4f}, write {f_write:.4f}",
-        f"algorithmic bytes per launch of {DOMINANT} in the stack (mean over qkv, o, gate|up): "
+        f"algorithmic bytes per launch of {DOMINANT} in the stack (mean over qkv, o, gate|up, down): "
         f"{float(np.mean(stack_bytes)):.0f}",
         "",
         f"@source_hash: {source_hash()}",
         f"@traffic_bytes_per_launch: {traffic:.0f}",
     ]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def trace_table(trace_dir, out_path):
+    """Per-kernel durations of every part of the hot path, from a rocprofv3
+    kernel trace of the default bench command."""
+    import csv
+
+    stats = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+        stats += list(csv.DictReader(open(f)))
+    lines = [
+        "rocprofv3 kernel-trace statistics of the default bench command (all parts of the hot path:",
+        "dense stack at M=1, 4, 16; FFN pair at M=1, 8, 64, 256; product-VQ at M=1, 16, 64; MoE block at M=32;",
+        "oracle timing on the host runs no GPU kernels).",
+        "",
+        "command (run from the repository root, cd /tmp && export TMPDIR=/tmp first):",
+        "  rocprofv3 --kernel-trace --stats -d <dir> -o k --output-format csv -- python3 bench.py",
+        "  python3 bench.py --trace-summary <dir> <this file>",
+        "",
+        f"  {'kernel':100s} {'calls':>7s} {'avg us':>10s} {'min us':>9s} {'total us':>12s}",
+    ]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"  {r['Name'][:100]:100s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} "
+                     f"{float(r['MinNs']) / 1e3:9.3f} {float(r['TotalDurationNs']) / 1e3:12.1f}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -505,9 +547,15 @@ def main():
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                     help="write the counter summary under profiles/ from rocprofv3 outputs, then exit")
     ap.add_argument("--summary-command", default="python3 bench.py --steps 5 --warmup 1 --no-extra --no-cpu")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "OUT"),
+                    help="write a per-kernel table of a rocprofv3 --kernel-trace --stats run of the default "
+                         "command (python3 bench.py) to OUT, then exit")
     args = ap.parse_args()
     if args.summarize:
         summarize(*args.summarize, args.summary_command, PROFILE_SUMMARY)
+        return
+    if args.trace_summary:
+        trace_table(*args.trace_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -538,14 +586,11 @@ def main():
     for sh in stack.shapes:
         d = np.array(per[sh["name"]])
         avg = float(d.mean())
-        fused = sh["K"] == 4096      # K <= 8192 at one token: one gemv_fold launch per call
         shape_stats[sh["name"]] = {"K": sh["K"], "N": sh["N"], "bytes": sh["bytes"], "avg_us": round(avg * 1e6, 3),
-                                   "GBps": round(sh["bytes"] / avg / 1e9, 1),
-                                   "kernels": "gemv_fold" if fused else "rotate + gemv_rtn"}
-        if fused:
-            dom_b += sh["bytes"] * len(d)
-            dom_t += float(d.sum())
-            dom_n += len(d)
+                                   "GBps": round(sh["bytes"] / avg / 1e9, 1), "kernels": "gemv_mfma"}
+        dom_b += sh["bytes"] * len(d)
+        dom_t += float(d.sum())
+        dom_n += len(d)
     achieved = dom_b / dom_t / 1e9
     log(f"[bench] per-launch: {json.dumps(shape_stats)}")
 

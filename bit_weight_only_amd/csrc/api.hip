@@ -52,12 +52,11 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return LBQ_ERR_ALIGN;
   if (ws_bytes < linear_ws_bytes(M, w->K, w->N)) return LBQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // the MFMA GEMM's decode costs the same at 4 tokens as at 16; below that the
-  // VALU GEMV is faster
-  const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 3);
-  // One or two tokens on short rows: rotation fused into the decoder, one launch.
-  if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_fold_supported(M, w->K) && aligned16(w->signs))
-    return hip_status(launch_gemv_fold(w->planes, w->meta, x, w->signs, y, M, w->K, w->N, w->bits, 0, 0, 0, s, ev0,
+  // up to four tokens share one matrix-core GEMV pass; from there on the MFMA GEMM
+  const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 4);
+  // One to four tokens: rotation fused into the matrix-core decoder, one launch.
+  if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_mfma_supported(M, w->K, w->N) && aligned16(w->signs))
+    return hip_status(launch_gemv_mfma(w->planes, w->meta, x, w->signs, y, M, w->K, w->N, w->bits, 0, 0, 0, s, ev0,
                                        ev1));
   uint16_t *xr = static_cast<uint16_t *>(ws);
   if (!gemv) {

@@ -32,6 +32,17 @@ hipError_t launch_gemv_fold(const void *planes, const void *meta, const uint16_t
                             int M, int K, int N, int bits, int lanes, int rb, int grid_cap, hipStream_t s,
                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
+// RTN dequant-GEMV on raw activations x [M][K] (1 <= M <= 4) on the matrix
+// cores (fp8 activation pieces x fp4 code operands), rotation fused into the
+// prologue: one launch, no workspace. x and signs must be 16-byte aligned.
+// grid / block / depth <= 0 take gemv_mfma_shape's choice; non-null events
+// take the kernel's own begin / end times.
+bool gemv_mfma_supported(int M, int K, int N);
+void gemv_mfma_shape(int M, int K, int N, int bits, int &grid, int &block, int &depth);
+hipError_t launch_gemv_mfma(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs,
+                            uint16_t *y, int M, int K, int N, int bits, int grid, int block, int depth,
+                            hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+
 // Product-VQ GEMV (M <= 16) and MFMA GEMM on rotated activations.
 hipError_t launch_gemv_pvq(const uint8_t *idx, const uint16_t *scale, const uint8_t *codebook, const uint16_t *xr,
                            uint16_t *y, int M, int K, int N, hipStream_t s);

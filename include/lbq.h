@@ -79,7 +79,7 @@ typedef enum {
   LBQ_FMT_PVQ_4x8 = 1
 } lbq_format;
 
-/* Kernel path for lbq_linear_forward_path. AUTO picks the GEMV for M <= 3 and
+/* Kernel path for lbq_linear_forward_path. AUTO picks the GEMV for M <= 4 and
  * the MFMA GEMM above (measured crossover); forcing the GEMV needs M <= 16. */
 typedef enum {
   LBQ_PATH_AUTO = 0,
@@ -143,10 +143,12 @@ lbq_status lbq_pack(const float *W, int32_t K, int32_t N, int32_t bits, int32_t 
 lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
 
 /* y[M][N] (fp16) = x[M][K] (fp16) W_hat^T, W_hat the weight w decodes to.
- * The activation rotation runs either inside the GEMV's prologue (one or two
- * tokens on rows of up to 8192 / 4096 inputs, signs 16-byte aligned) or as its
- * own launch into the workspace, followed by the dequant-GEMV (M <= 3) or the
- * MFMA dequant-GEMM (M >= 4). Accumulation is fp32. */
+ * The activation rotation runs either inside the GEMV's prologue (RTN codes,
+ * signs 16-byte aligned: one to four tokens on the matrix cores when K is a
+ * multiple of 512, else one or two tokens on rows of up to 8192 / 4096 inputs)
+ * or as its own launch into the workspace, followed by the dequant-GEMV
+ * (M <= 4) or the MFMA dequant-GEMM (M >= 5). Accumulation is fp32. The result
+ * of a call does not depend on timing: repeat calls give identical bits. */
 lbq_status lbq_linear_forward(const lbq_weight *w, const uint16_t *x, int32_t M,
                               uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 

@@ -83,6 +83,23 @@ def test_gemv_small_shapes(L, dev, bits, n, k, m):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("n,k", [(17, 512), (300, 1536), (1030, 2048), (4100, 512), (33, 16384)])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_gemv_matrix_core_tokens(L, dev, bits, n, k, m):
+    """One to four tokens with K a multiple of 512 run the matrix-core GEMV
+    (fp8 activation pieces x fp4 codes, rotation in the prologue): ragged N,
+    fewer tiles than workgroups (n = 17, 300), more (n = 4100, 257 tiles),
+    long rows (K = 16384, 128 groups), every token count it serves."""
+    say(f"gemv mfma bits={bits} n={n} k={k} m={m}")
+    w, s, planes, meta, pl = make_rtn(n, k, bits, 17, n + k + bits)
+    x = synth.activations(m, k, workload=17, item=m)
+    y = L.linear_forward(pl, to_dev(x, dev)).cpu().numpy().astype(np.float64)
+    rows = np.arange(n) if n <= 1100 else sample_rows(n, 48, seed=m)
+    want = oracle_rtn_rows(w, s, bits, x, rows)
+    assert O.rel_l2(y[:, rows], want) < TOL
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("n,k", [(257, 4096), (130, 5120), (67, 8192)])
 @pytest.mark.parametrize("m", [1, 2])
 def test_gemv_fused_and_staged_rotation_agree(L, dev, bits, n, k, m):

@@ -70,6 +70,20 @@ def test_rotation_is_orthogonal():
     np.testing.assert_allclose(O.inverse_rotate(O.rotate(v, s), s), v, atol=1e-14)
 
 
+def test_rotated_group_sum_is_scaled_first_signed_input():
+    """Sylvester's H_128 has column sums 128, 0, ..., 0, so the sum of one rotated
+    128-block is 128 / sqrt(128) * s_0 * x_0: the matrix-core GEMV takes its
+    per-group activation sum from this identity instead of a reduction."""
+    h = O.hadamard(128)
+    np.testing.assert_array_equal(h.sum(axis=0), np.r_[128.0, np.zeros(127)])
+    k = 1024
+    s = synth.signs(k, workload=9, item=3)
+    v = np.random.default_rng(4).standard_normal((3, k))
+    got = O.rotate(v, s).reshape(3, k // 128, 128).sum(axis=2)
+    want = math.sqrt(128.0) * (s * v).reshape(3, k // 128, 128)[:, :, 0]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
 def test_rotated_basis_product_equals_plain_product():
     k, n, m = 512, 7, 3
     s = synth.signs(k, workload=9, item=2)
