@@ -33,11 +33,19 @@ lbq_status check_weight(const lbq_weight *w) {
   return LBQ_OK;
 }
 
-size_t linear_ws_bytes(int M, int K, int N) {
-  // the rotated activations, their per-(group, token) sums, then the GEMM's
-  // split-K partial tiles and counters
-  return round_up(static_cast<size_t>(M) * K * 2, kAlign) + round_up(static_cast<size_t>(M) * (K / 128) * 8, kAlign) +
-         gemm_scratch_bytes(gemm_plan(M, K, N));
+GemmPlan linear_gemm_plan(const lbq_weight *w, int M) {
+  return w->format == LBQ_FMT_RTN_PLANES ? gemm_rtn_plan(M, w->K, w->N) : gemm_plan(M, w->K, w->N);
+}
+
+size_t tz_bytes(const lbq_weight *w, int M) {
+  return w->format == LBQ_FMT_RTN_PLANES ? round_up(static_cast<size_t>(M) * gemm_tz_stride(w->K) * 4, kAlign) : 0;
+}
+
+size_t linear_ws_bytes(const lbq_weight *w, int M) {
+  // the rotated activations, the RTN GEMM's per-(token, group) sums, then the
+  // GEMM's split-K partial tiles and counters
+  return round_up(static_cast<size_t>(M) * w->K * 2, kAlign) + tz_bytes(w, M) +
+         gemm_scratch_bytes(linear_gemm_plan(w, M));
 }
 
 lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint16_t *y, void *ws, size_t ws_bytes,
@@ -50,7 +58,7 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
   if (M == 0) return LBQ_OK;
   if (!x || !y || !ws) return LBQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return LBQ_ERR_ALIGN;
-  if (ws_bytes < linear_ws_bytes(M, w->K, w->N)) return LBQ_ERR_WORKSPACE;
+  if (ws_bytes < linear_ws_bytes(w, M)) return LBQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // up to four tokens share one matrix-core GEMV pass; from there on the MFMA GEMM
   const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 4);
@@ -60,18 +68,23 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
                                        ev1));
   uint16_t *xr = static_cast<uint16_t *>(ws);
   if (!gemv) {
-    // MFMA GEMM: rotation into the folded order (clearing the split-K counters), then the GEMM
-    const GemmPlan gp = gemm_plan(M, w->K, w->N);
-    float2 *sums =
-        reinterpret_cast<float2 *>(static_cast<uint8_t *>(ws) + round_up(static_cast<size_t>(M) * w->K * 2, kAlign));
-    void *scratch = reinterpret_cast<uint8_t *>(sums) + round_up(static_cast<size_t>(M) * (w->K / 128) * 8, kAlign);
-    if (launch_rotate_folded(x, M, w->K, w->signs, w->bits, xr, sums, gemm_counter_ptr(gp, scratch),
-                             gemm_counters(gp), s) != hipSuccess)
+    // MFMA GEMM: rotation into the folded order (with the RTN zero-point sums,
+    // clearing the split-K counters), then the GEMM
+    const bool rtn = w->format == LBQ_FMT_RTN_PLANES;
+    if (rtn && !gemm_rtn_supported(w->K, w->N, w->bits)) return LBQ_ERR_SHAPE;
+    const GemmPlan gp = linear_gemm_plan(w, M);
+    uint8_t *after_x = static_cast<uint8_t *>(ws) + round_up(static_cast<size_t>(M) * w->K * 2, kAlign);
+    uint32_t *tz = rtn ? reinterpret_cast<uint32_t *>(after_x) : nullptr;
+    void *scratch = after_x + tz_bytes(w, M);
+    if (launch_rotate_folded(x, M, w->K, w->signs, xr, tz, gemm_counter_ptr(gp, scratch), gemm_counters(gp), s) !=
+        hipSuccess)
       return LBQ_ERR_HIP;
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return LBQ_ERR_HIP;
-    if (launch_gemm(gp, w->format, w->bits, w->planes, w->meta, static_cast<const uint8_t *>(w->codebook), xr, sums, y,
-                    M, w->K, w->N, scratch, s) != hipSuccess)
-      return LBQ_ERR_HIP;
+    const hipError_t ge =
+        rtn ? launch_gemm_rtn(gp, w->bits, w->planes, w->meta, xr, tz, y, M, w->K, w->N, scratch, s)
+            : launch_gemm_pvq(gp, w->planes, w->meta, static_cast<const uint8_t *>(w->codebook), xr, y, M, w->K, w->N,
+                              scratch, s);
+    if (ge != hipSuccess) return LBQ_ERR_HIP;
     return (ev1 && hipEventRecord(ev1, s) != hipSuccess) ? LBQ_ERR_HIP : LBQ_OK;
   }
   hipError_t e = launch_rotate(x, M, w->K, w->signs, xr, s);
@@ -145,7 +158,7 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes) {
   lbq_status st = check_weight(w);
   if (st != LBQ_OK) return st;
   if (M < 0) return LBQ_ERR_SHAPE;
-  *bytes = linear_ws_bytes(M, w->K, w->N);
+  *bytes = linear_ws_bytes(w, M);
   return LBQ_OK;
 }
 

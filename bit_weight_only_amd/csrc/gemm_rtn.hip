@@ -1,0 +1,408 @@
+// MFMA dequant-GEMM for RTN codes: y = x' W'^T with W' = s (q - z) per
+// 128-group (Qwen3-8B BPDQ model card, group-wise scale and zero), decoded
+// inside the K mainloop into the B operand of v_mfma_f32_16x16x32_f16 (no
+// expand-to-dense round trip through memory, the gap the Laguna-S-2.1 card
+// names for its prefill path in "Reading it honestly").
+//
+// B = round_fp16(s q). A code q of slot class m OR-ed into the mantissa of fp16
+// 2^(10 - m) is exactly h = 2^(10 - m) + q, and one v_pk_fma_f16
+// h * s + (-s 2^(10 - m)) is round(s q) for two weights at once: inside the
+// fused operation h * s is exact and the addend cancels the offset exactly.
+// So each pair of weights costs two VALU operations (mask-insert, fma) and the
+// accumulators run through the whole K range with no per-group rescaling.
+// Every class sits at mantissa bit 4 or above (offsets 64, 16, 4), which keeps
+// the addends finite for every scale below 2^10.
+// The zero-point term -s z T_g (T_g = sum of the group's rotated activations)
+// is one MFMA per 16 groups at the end of the slice: A holds (T_g/16 high,
+// T_g/16 low) fp16 pairs per (token, group), B the pairs (-16 s z, -16 s z).
+//
+// Tiling: a workgroup of 4 wavefronts owns 64 NB output rows and 16 MT tokens;
+// wave w owns NB blocks of 16 rows, so each A fragment read from LDS feeds NB
+// MFMAs. The workgroup's K range is one of S slices of the 128-groups (split-K
+// when the tile grid alone leaves the chip idle). Per group:
+//  * the token tile's rotated activations (folded slot order: u32 slot c of a
+//    32-chunk = (x[c], x[c + 16])) are copied global -> LDS asynchronously into
+//    a ring of kRing slots, kRing - 1 groups ahead, one barrier per group;
+//  * each wave's code vectors and (s, z) words go straight into registers by
+//    buffer loads, kRing - 1 groups ahead (offsets past the end return zeros
+//    without a memory access: rows past N, groups past the slice); a 4x4 lane
+//    transpose gives lane (j, kq) word column kq of every plane of its rows;
+//  * for k-step t, lane (i, kq) supplies slots 4t..4t+3 of token i's chunk kq
+//    as A and slots 4t..4t+3 of row j's word column kq as B, so both operands
+//    agree on which k each element is.
+// Split-K: each workgroup writes its fp32 partial tile to the workspace; the
+// last of the S workgroups of a tile to arrive (an atomic counter the rotation
+// launch cleared) sums the S partials in slice order and writes y, so the
+// result does not depend on arrival order. No workgroup ever waits on another.
+#include "device.h"
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace lbq {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 3;                        // activation slots; loads run kRing - 1 groups ahead
+constexpr int kBufferFlags = 0x00020000;        // buffer descriptor word 3 (32-bit data, no swizzle)
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every supported size
+
+struct RtnGemmArgs {
+  const uint4 *xf;         // rotated activations [M][K] fp16, folded slot order
+  const uint4 *tz;         // [M][Gp / 4] of 4 u32: (T/16 high, T/16 low) fp16 per (token, group)
+  const uint4 *planes;     // [N][G][BITS] 16-byte plane vectors
+  const uint32_t *meta;    // [N][G] (fp16 s, fp16 z)
+  uint16_t *y;             // [M][N]
+  float *part;             // split-K partial tiles (S > 1)
+  uint32_t *counters;      // split-K arrival counters, one per tile, zero on entry
+  int M, K, N, S, Gp;
+};
+
+__device__ __forceinline__ uint32_t pk_fma(uint32_t h, half2_t s2, half2_t c) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, h), s2, c));
+}
+
+// Slot classes. 2-bit: slot 2p / 2p + 1 is field p of the even / odd merged
+// word; fields 2..4 sit at mantissa bits 4, 6, 8, fields 5..7 land there after
+// a shift right by 6 and fields 0, 1 at bits 4, 6 after a shift left by 4.
+// Class index (m - 4) / 2. 3/4-bit: nibble i of the merged nibble words, moved
+// to bits 4..7 (class 0, m = 4) by a shift of 4 - 4i.
+template <int BITS>
+__host__ __device__ constexpr int gemm_slot_class(int c) {
+  if constexpr (BITS == 2) {
+    constexpr int kField[8] = {0, 1, 0, 1, 2, 0, 1, 2};
+    return kField[c >> 1];
+  } else {
+    return 0;
+  }
+}
+template <int BITS>
+constexpr int gemm_num_classes() {
+  return BITS == 2 ? 3 : 1;
+}
+
+// Biased decode of one 32-code word column into the 16 slots (fp16 pairs
+// 2^(10 - m) + q for the codes of positions c and c + 16).
+template <int BITS>
+__device__ __forceinline__ void decode_biased(const uint32_t *w, uint32_t h[16]) {
+  if constexpr (BITS == 2) {
+    uint32_t e, o;
+    merge2(w[0], w[1], e, o);
+    const uint32_t el = e << 4, ol = o << 4, er = e >> 6, orr = o >> 6;
+    const uint32_t c4 = biased_one2(4), c6 = biased_one2(6), c8 = biased_one2(8);
+    h[0] = and_or(el, 0x00300030u, c4);
+    h[1] = and_or(ol, 0x00300030u, c4);
+    h[2] = and_or(el, 0x00C000C0u, c6);
+    h[3] = and_or(ol, 0x00C000C0u, c6);
+    h[4] = and_or(e, 0x00300030u, c4);
+    h[5] = and_or(o, 0x00300030u, c4);
+    h[6] = and_or(e, 0x00C000C0u, c6);
+    h[7] = and_or(o, 0x00C000C0u, c6);
+    h[8] = and_or(e, 0x03000300u, c8);
+    h[9] = and_or(o, 0x03000300u, c8);
+    h[10] = and_or(er, 0x00300030u, c4);
+    h[11] = and_or(orr, 0x00300030u, c4);
+    h[12] = and_or(er, 0x00C000C0u, c6);
+    h[13] = and_or(orr, 0x00C000C0u, c6);
+    h[14] = and_or(er, 0x03000300u, c8);
+    h[15] = and_or(orr, 0x03000300u, c8);
+  } else {
+    uint32_t n[4];
+    merge_nibbles<BITS>(w, n);
+    const uint32_t c4 = biased_one2(4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      h[r] = and_or(n[r] << 4, 0x00F000F0u, c4);
+      h[4 + r] = and_or(n[r], 0x00F000F0u, c4);
+      h[8 + r] = and_or(n[r] >> 4, 0x00F000F0u, c4);
+      h[12 + r] = and_or(n[r] >> 8, 0x00F000F0u, c4);
+    }
+  }
+}
+
+// The ring slots are separate LDS objects so the compiler can tell that a read
+// of one slot does not depend on the copies in flight into the others.
+template <int BITS, int NB, int MT>
+__global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
+  constexpr int U = NB * BITS;           // 16-byte plane vectors of a wave's rows per group
+  constexpr int T = (U + 3) / 4;         // of them per lane
+  constexpr int D = kRing - 1;           // groups in flight
+  constexpr int CA = MT;                 // activation copies per wave per group (16 MT rows x 256 B)
+  constexpr int kLoads = CA + T + NB;    // vector-memory operations per wave per group
+  constexpr int C = gemm_num_classes<BITS>();
+  __shared__ __attribute__((aligned(16))) uint4 xs0[16 * MT * 16];
+  __shared__ __attribute__((aligned(16))) uint4 xs1[16 * MT * 16];
+  __shared__ __attribute__((aligned(16))) uint4 xs2[16 * MT * 16];
+  uint4 *const xs[kRing] = {xs0, xs1, xs2};
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane & 15, kq = lane >> 4;
+  const int G = a.K / kGroup;
+  const int split = blockIdx.x;
+  const int tile_id = blockIdx.z * gridDim.y + blockIdx.y;
+  const int row0 = blockIdx.y * (kWaves * 16 * NB) + wave * 16 * NB + j;   // the lane's row of block 0
+  const int m0 = blockIdx.z * (16 * MT);
+  const int g0 = static_cast<int>((static_cast<long>(split) * G) / a.S);
+  const int g1 = static_cast<int>((static_cast<long>(split + 1) * G) / a.S);
+
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4 *>(a.planes), 0, a.N * G * BITS * 16, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t mrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(a.meta), 0, a.N * G * 4, kBufferFlags);
+
+  // lane (j, kq) loads plane vectors u = kq + 4t of its rows: block u / BITS, plane u % BITS
+  uint32_t poff[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int u = kq + 4 * t;
+    const int row = row0 + (u / BITS) * 16;
+    poff[t] = (u < U && row < a.N) ? (static_cast<uint32_t>(row) * G * BITS + u % BITS) * 16 : kOutOfRange;
+  }
+  uint32_t moff[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int row = row0 + nb * 16;
+    moff[nb] = row < a.N ? static_cast<uint32_t>(row) * G * 4 : kOutOfRange;
+  }
+  // activation copies: wave w fills physical vectors [64 CA w, 64 CA (w + 1)) of
+  // a slot. Logical column c of token t sits at physical column c ^ (t & 15), so
+  // the 16-byte reads of 16 consecutive tokens at one column (one pass of a
+  // ds_read_b128) hit 16 distinct bank groups. Tokens past M repeat token M - 1
+  // (their outputs are never stored).
+  const uint4 *asrc[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int p = 64 * (CA * wave + i) + lane;
+    const int tok = p >> 4, c = (p & 15) ^ (tok & 15);
+    asrc[i] = a.xf + static_cast<size_t>(min(m0 + tok, a.M - 1)) * (a.K / 8) + c;
+  }
+
+  uint4 bv[kRing][T];
+  uint32_t mv[kRing][NB];
+  float4_t acc[NB][MT];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // loads of group g into ring slot q (past the slice: the activation copies
+  // repeat the slice's last group, the code and meta loads return zeros)
+  auto issue = [&](int q, int g) {
+    const int gc = min(g, g1 - 1);
+#pragma unroll
+    for (int i = 0; i < CA; ++i) copy16_to_lds(asrc[i] + static_cast<size_t>(gc) * 16, xs[q] + 64 * (CA * wave + i));
+    const uint32_t past = g < g1 ? 0u : kOutOfRange;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      bv[q][t] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, (poff[t] | past) + g * (BITS * 16), 0, 0));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      mv[q][nb] = __builtin_amdgcn_raw_buffer_load_b32(mrs, (moff[nb] | past) + g * 4, 0, 0);
+  };
+
+  auto contract = [&](int q) {
+    uint32_t w[4 * T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      uint32_t e0 = bv[q][t].x, e1 = bv[q][t].y, e2 = bv[q][t].z, e3 = bv[q][t].w;
+      transpose4(e0, e1, e2, e3);
+      w[4 * t] = e0;
+      w[4 * t + 1] = e1;
+      w[4 * t + 2] = e2;
+      w[4 * t + 3] = e3;
+    }
+    half2_t s2[NB], nc[NB][C];
+    uint32_t h[NB][16];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const _Float16 s = __builtin_bit_cast(half2_t, mv[q][nb])[0];
+      s2[nb] = half2_t{s, s};
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const _Float16 off = static_cast<_Float16>(-static_cast<float>(1 << (6 - 2 * c)));   // -2^(10 - m)
+        nc[nb][c] = s2[nb] * half2_t{off, off};
+      }
+      decode_biased<BITS>(&w[nb * BITS], h[nb]);
+    }
+    const uint4 *slot = xs[q];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      half8_t av[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int tok = mt * 16 + j;
+        av[mt] = __builtin_bit_cast(half8_t, slot[tok * 16 + ((4 * kq + t) ^ j)]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          b[e] = pk_fma(h[nb][4 * t + e], s2[nb], nc[nb][gemm_slot_class<BITS>(4 * t + e)]);
+        const half8_t bop = __builtin_bit_cast(half8_t, make_uint4(b[0], b[1], b[2], b[3]));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], bop, acc[nb][mt], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int q = 0; q < D; ++q) issue(q, g0 + q);
+  for (int g = g0; g < g1; g += kRing) {
+#pragma unroll
+    for (int q = 0; q < kRing; ++q) {
+      // group g + q: its loads are the oldest kLoads of this wave's D groups in
+      // flight; after the barrier every wave's copies are in LDS and every wave
+      // is done reading the slot refilled next
+      wait_vm_lds<(D - 1) * kLoads>();
+      __builtin_amdgcn_s_barrier();
+      issue((q + D) % kRing, g + q + D);
+      if (g + q < g1) contract(q);
+    }
+  }
+
+  // zero-point term of the slice: K = (group, high/low) over 16 groups per MFMA;
+  // lane (j, kq) covers groups 16 c + 4 kq .. + 3
+  for (int c16 = g0 / 16; c16 <= (g1 - 1) / 16; ++c16) {
+    half8_t za[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int tok = min(m0 + mt * 16 + j, a.M - 1);
+      za[mt] = __builtin_bit_cast(half8_t, a.tz[static_cast<size_t>(tok) * (a.Gp / 4) + 4 * c16 + kq]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      uint32_t b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int g = 16 * c16 + 4 * kq + e;
+        const half2_t sz = __builtin_bit_cast(half2_t, __builtin_amdgcn_raw_buffer_load_b32(mrs, moff[nb] + g * 4, 0, 0));
+        const _Float16 v = (g >= g0 && g < g1) ? static_cast<_Float16>(-16.0f) * (sz[0] * sz[1]) : static_cast<_Float16>(0.0f);
+        b[e] = __builtin_bit_cast(uint32_t, half2_t{v, v});
+      }
+      const half8_t bop = __builtin_bit_cast(half8_t, make_uint4(b[0], b[1], b[2], b[3]));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(za[mt], bop, acc[nb][mt], 0, 0, 0);
+    }
+  }
+  wait_vm_lds<0>();   // no copy into LDS may outlive the workgroup
+
+  if (a.S > 1) {
+    // publish this slice's partial tile; the last slice to arrive sums them all
+    constexpr int kTileFloats = NB * MT * 4 * kThreads;
+    float *mine = a.part + (static_cast<size_t>(tile_id) * a.S + split) * kTileFloats + threadIdx.x;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) store_coherent(mine + ((nb * MT + mt) * 4 + r) * kThreads, acc[nb][mt][r]);
+    wait_vm_lds<0>();   // the stores above have completed
+    __syncthreads();
+    __shared__ uint32_t last;
+    if (threadIdx.x == 0)
+      last = (__hip_atomic_fetch_add(a.counters + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              static_cast<uint32_t>(a.S - 1))
+                 ? 1u
+                 : 0u;
+    __syncthreads();
+    if (!last) return;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < a.S; ++s2) {
+      float *src = a.part + (static_cast<size_t>(tile_id) * a.S + s2) * kTileFloats + threadIdx.x;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nb][mt][r] += load_coherent(src + ((nb * MT + mt) * 4 + r) * kThreads);
+    }
+  }
+
+  // D layout: lane holds tokens 4 kq + r (r = 0..3) of token tile mt, row j of block nb
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int row = row0 + nb * 16;
+    if (row < a.N) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = m0 + mt * 16 + kq * 4 + r;
+          if (tok < a.M) a.y[static_cast<size_t>(tok) * a.N + row] = f32_to_f16_bits(acc[nb][mt][r]);
+        }
+      }
+    }
+  }
+}
+
+template <int BITS, int NB, int MT>
+void launch_rtn(dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_rtn_kernel<BITS, NB, MT>), grid, dim3(kThreads), 0, s, a);
+}
+
+template <int BITS>
+void launch_rtn_bits(const GemmPlan &p, dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
+  if (p.nb == 4) {
+    if (p.mt == 1) launch_rtn<BITS, 4, 1>(grid, a, s);
+    else if (p.mt == 2) launch_rtn<BITS, 4, 2>(grid, a, s);
+    else launch_rtn<BITS, 4, 4>(grid, a, s);
+  } else if (p.nb == 2) {
+    if (p.mt == 1) launch_rtn<BITS, 2, 1>(grid, a, s);
+    else if (p.mt == 2) launch_rtn<BITS, 2, 2>(grid, a, s);
+    else launch_rtn<BITS, 2, 4>(grid, a, s);
+  } else {
+    if (p.mt == 1) launch_rtn<BITS, 1, 1>(grid, a, s);
+    else if (p.mt == 2) launch_rtn<BITS, 1, 2>(grid, a, s);
+    else launch_rtn<BITS, 1, 4>(grid, a, s);
+  }
+}
+
+}  // namespace
+
+int gemm_tz_stride(int K) {
+  return (K / kGroup + 15) / 16 * 16;
+}
+
+bool gemm_rtn_supported(int K, int N, int bits) {
+  // 32-bit buffer offsets over the planes and meta words
+  return static_cast<long long>(N) * (K / kGroup) * bits * 16 < static_cast<long long>(kOutOfRange) - 4096;
+}
+
+hipError_t launch_gemm_rtn(const GemmPlan &p, int bits, const void *planes, const void *meta, const uint16_t *xf,
+                           const uint32_t *tz, uint16_t *y, int M, int K, int N, void *scratch, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if ((p.nb != 1 && p.nb != 2 && p.nb != 4) || (p.mt != 1 && p.mt != 2 && p.mt != 4) || p.S < 1)
+    return hipErrorInvalidValue;
+  if (bits < 2 || bits > 4 || !gemm_rtn_supported(K, N, bits)) return hipErrorInvalidValue;
+  RtnGemmArgs a;
+  a.xf = reinterpret_cast<const uint4 *>(xf);
+  a.tz = reinterpret_cast<const uint4 *>(tz);
+  a.planes = static_cast<const uint4 *>(planes);
+  a.meta = static_cast<const uint32_t *>(meta);
+  a.y = y;
+  a.part = static_cast<float *>(scratch);
+  a.counters = gemm_counter_ptr(p, scratch);
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.S = p.S;
+  a.Gp = gemm_tz_stride(K);
+  const dim3 grid(static_cast<unsigned>(p.S), static_cast<unsigned>(p.n_tiles), static_cast<unsigned>(p.m_tiles));
+  switch (bits) {
+    case 2: launch_rtn_bits<2>(p, grid, a, s); break;
+    case 3: launch_rtn_bits<3>(p, grid, a, s); break;
+    default: launch_rtn_bits<4>(p, grid, a, s); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lbq

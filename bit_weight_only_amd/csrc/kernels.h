@@ -11,11 +11,11 @@ namespace lbq {
 
 hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, hipStream_t s);
 // Rotation into the folded slot order (u32 slot c of each 32-chunk holds
-// (x'[c], x'[c+16])), with the per-(group, token) sums sums[g * M + m] =
-// (P, T) the GEMM's code decode needs for code width `bits`; also zeroes
-// n_counters u32 at counters.
-hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, int bits, uint16_t *out,
-                                float2 *sums, uint32_t *counters, int n_counters, hipStream_t s);
+// (x'[c], x'[c+16])); with tz non-null also the RTN GEMM's per-(token, group)
+// sums tz[m * gemm_tz_stride(K) + g] = (T/16 high, T/16 low) fp16, zero-padded;
+// also zeroes n_counters u32 at counters.
+hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, uint32_t *tz,
+                                uint32_t *counters, int n_counters, hipStream_t s);
 
 // RTN dequant-GEMV for 1 <= M <= 16 on already-rotated activations xr [M][K].
 hipError_t launch_gemv_rtn(const void *planes, const void *meta, const uint16_t *xr, uint16_t *y, int M, int K,
@@ -43,25 +43,30 @@ hipError_t launch_gemv_mfma(const void *planes, const void *meta, const uint16_t
                             uint16_t *y, int M, int K, int N, int bits, int grid, int block, int depth,
                             hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
-// Product-VQ GEMV (M <= 16) and MFMA GEMM on rotated activations.
+// Product-VQ GEMV (M <= 16) on rotated activations.
 hipError_t launch_gemv_pvq(const uint8_t *idx, const uint16_t *scale, const uint8_t *codebook, const uint16_t *xr,
                            uint16_t *y, int M, int K, int N, hipStream_t s);
-// MFMA dequant-GEMM (RTN planes, format 0, or product-VQ, format 1) on
-// activations rotated into the folded slot order (launch_rotate_folded). The
-// plan fixes the tiling and the split-K count; split-K needs
-// gemm_scratch_bytes(plan) of scratch whose arrival counters
-// (gemm_counter_ptr, gemm_counters of them) are zero when the GEMM starts.
+// MFMA dequant-GEMMs on activations rotated into the folded slot order
+// (launch_rotate_folded): RTN planes (gemm_rtn_plan, launch_gemm_rtn, with the
+// rotation's tz sums) and product-VQ (gemm_plan, launch_gemm_pvq). A plan fixes
+// the tiling (nb row blocks of 16 per wave, mt token tiles of 16) and the
+// split-K count; split-K needs gemm_scratch_bytes(plan) of scratch whose
+// arrival counters (gemm_counter_ptr, gemm_counters of them) are zero when the
+// GEMM starts.
 struct GemmPlan {
   int nb, mt, S, n_tiles, m_tiles;
 };
 GemmPlan gemm_plan(int M, int K, int N);
+GemmPlan gemm_rtn_plan(int M, int K, int N);
 size_t gemm_scratch_bytes(const GemmPlan &p);
 int gemm_counters(const GemmPlan &p);
 uint32_t *gemm_counter_ptr(const GemmPlan &p, void *scratch);
-hipError_t launch_gemm(const GemmPlan &p, int format, int bits, const void *planes, const void *meta,
-                       const uint8_t *codebook, const uint16_t *xf, const float2 *sums, uint16_t *y, int M, int K,
-                       int N, void *scratch, hipStream_t s);
-
+int gemm_tz_stride(int K);
+bool gemm_rtn_supported(int K, int N, int bits);
+hipError_t launch_gemm_rtn(const GemmPlan &p, int bits, const void *planes, const void *meta, const uint16_t *xf,
+                           const uint32_t *tz, uint16_t *y, int M, int K, int N, void *scratch, hipStream_t s);
+hipError_t launch_gemm_pvq(const GemmPlan &p, const void *idx, const void *row_scale, const uint8_t *codebook,
+                           const uint16_t *xf, uint16_t *y, int M, int K, int N, void *scratch, hipStream_t s);
 
 hipError_t launch_unpack_rtn(const void *planes, int K, int N, int bits, uint8_t *codes, hipStream_t s);
 

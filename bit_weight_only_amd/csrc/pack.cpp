@@ -151,7 +151,8 @@ lbq_status pack_rtn(const float *W, int K, int N, int bits, const int8_t *signs,
           if (u[i] > mx) mx = u[i];
         }
         uint16_t s16 = f64_to_f16_rne((mx - mn) / L);
-        if ((s16 & 0x7FFFu) == 0x7C00u) {
+        // the GEMM's decode needs finite -64 s and -16 s z in fp16: s < 128
+        if ((s16 & 0x7FFFu) >= 0x5800u) {
           err = LBQ_ERR_RANGE;
           return;
         }

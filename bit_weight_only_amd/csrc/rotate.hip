@@ -32,19 +32,19 @@ __global__ void __launch_bounds__(256) rotate_kernel(const uint32_t *__restrict_
                             (static_cast<uint32_t>(f32_to_f16_bits(v1 * c)) << 16);
 }
 
-// Same rotation, written in the folded slot order the MFMA GEMM stages: in
+// Same rotation, written in the folded slot order the MFMA GEMMs stage: in
 // each 32-element chunk, u32 slot c holds (x'[c], x'[c + 16]). Lane l and lane
 // l ^ 8 hold the two halves of the same slots and swap one value, so every lane
-// writes one whole slot. Per (group g, token m) it also writes the sums the
-// GEMM's decode needs, sums[g * M + m] = (P, T): P = sum_k 2^(10 - m_k) x'_k
-// over the slot classes m_k of the weight's code width, T = sum_k x'_k, both
-// of the fp16-rounded x'. And it clears n_counters u32 counters (the GEMM's
+// writes one whole slot. With tz non-null it also writes, per (token m, group
+// g), the group sum T = sum_k x'_k of the fp16-rounded x' as the fp16 pair
+// (T/16 rounded, the rounding of what is left) at tz[m * Gp + g], Gp = K/128
+// rounded up to a multiple of 16, and zero pairs for g in [K/128, Gp): the RTN
+// GEMM's zero-point term. It clears n_counters u32 counters (the GEMM's
 // split-K arrival counters) before the GEMM launch that uses them.
-template <int BITS>
 __global__ void __launch_bounds__(256) rotate_folded_kernel(const uint32_t *__restrict__ x,
                                                             const int8_t *__restrict__ signs,
-                                                            uint32_t *__restrict__ out, float2 *__restrict__ sums,
-                                                            int M, int K, uint32_t *__restrict__ counters,
+                                                            uint32_t *__restrict__ out, uint32_t *__restrict__ tz,
+                                                            int M, int K, int Gp, uint32_t *__restrict__ counters,
                                                             int n_counters) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n_counters; i += gridDim.x * 256) counters[i] = 0;
   const int lane = threadIdx.x & 63;
@@ -67,26 +67,29 @@ __global__ void __launch_bounds__(256) rotate_folded_kernel(const uint32_t *__re
   const uint32_t word = hi ? (got | (r1 << 16)) : (r0 | (got << 16));
   const int slot = ((2 * lane) & 15) + (hi ? 1 : 0);
   out[(base >> 1) + (lane >> 4) * 16 + slot] = word;
-  // slots 2l & 15 and its successor share one class
-  const float pair = f16_bits_to_f32(r0) + f16_bits_to_f32(r1);
-  float P = slot_weight<BITS>((2 * lane) & 15) * pair, T = pair;
+  if (!tz) return;
+  float T = f16_bits_to_f32(r0) + f16_bits_to_f32(r1);
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    P += __shfl_xor(P, off);
-    T += __shfl_xor(T, off);
+  for (int off = 1; off < 64; off <<= 1) T += __shfl_xor(T, off);
+  uint32_t *row = tz + static_cast<long>(m) * Gp;
+  if (lane == 0) {
+    const float t16 = T * 0.0625f;
+    const uint32_t th = f32_to_f16_bits(t16);
+    const uint32_t tl = f32_to_f16_bits(t16 - f16_bits_to_f32(th));
+    row[b] = th | (tl << 16);
   }
-  if (lane == 0) sums[static_cast<long>(b) * M + m] = make_float2(P, T);
+  if (b == blocks_per_row - 1)
+    for (int g = blocks_per_row + lane; g < Gp; g += 64) row[g] = 0;
 }
 
-hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, int bits, uint16_t *out,
-                                float2 *sums, uint32_t *counters, int n_counters, hipStream_t s) {
+hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, uint32_t *tz,
+                                uint32_t *counters, int n_counters, hipStream_t s) {
   const long nblk = static_cast<long>(M) * (K / kGroup);
   const long need = std::max<long>((nblk + 3) / 4, (n_counters + 255) / 256);
   if (need == 0) return hipSuccess;
-  auto kern = bits == 2 ? rotate_folded_kernel<2> : rotate_folded_kernel<4>;   // 3 and 4 bits share classes
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(need)), dim3(256), 0, s,
-                     reinterpret_cast<const uint32_t *>(x), signs, reinterpret_cast<uint32_t *>(out), sums, M, K,
-                     counters, n_counters);
+  hipLaunchKernelGGL(rotate_folded_kernel, dim3(static_cast<unsigned>(need)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t *>(x), signs, reinterpret_cast<uint32_t *>(out), tz, M, K,
+                     gemm_tz_stride(K), counters, n_counters);
   return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ typedef enum {
   LBQ_ERR_BITS = -3,       /* bits outside {2,3,4} (RTN) or != 2 (PVQ) */
   LBQ_ERR_ALIGN = -4,      /* a pointer that must be 16-byte aligned is not */
   LBQ_ERR_WORKSPACE = -5,  /* workspace smaller than the *_workspace query returned */
-  LBQ_ERR_RANGE = -6,      /* packing: non-finite weight or a scale that overflows fp16 */
+  LBQ_ERR_RANGE = -6,      /* packing: non-finite weight or an RTN group scale of 128 or more */
   LBQ_ERR_HIP = -7,        /* a HIP launch reported an error */
   LBQ_ERR_FORMAT = -8      /* unknown format, or a format the entry point does not take */
 } lbq_status;
@@ -134,7 +134,9 @@ lbq_status lbq_packed_bytes(int32_t K, int32_t N, int32_t bits, int32_t format,
  * PVQ (bits 2): rotate, s_n = fp16_rne(rms(w'_n) / rms(C)) (0 -> 1), and per
  * 4-weight half the nearest codebook entry to w'/s_n (squared distance,
  * ties to the lower index).
- * Returns LBQ_ERR_RANGE for non-finite W or an fp16 overflow of a scale. */
+ * Returns LBQ_ERR_RANGE for non-finite W, a PVQ scale that overflows fp16, or
+ * an RTN scale s >= 128 (the MFMA GEMM's decode holds -64 s and -16 s z in
+ * fp16; a group would need a weight range of 128 (2^b - 1) to reach it). */
 lbq_status lbq_pack(const float *W, int32_t K, int32_t N, int32_t bits, int32_t format,
                     const int8_t *signs, const uint8_t *codebook,
                     void *planes_out, void *meta_out);
@@ -147,8 +149,11 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
  * signs 16-byte aligned: one to four tokens on the matrix cores when K is a
  * multiple of 512, else one or two tokens on rows of up to 8192 / 4096 inputs)
  * or as its own launch into the workspace, followed by the dequant-GEMV
- * (M <= 4) or the MFMA dequant-GEMM (M >= 5). Accumulation is fp32. The result
- * of a call does not depend on timing: repeat calls give identical bits. */
+ * (M <= 4) or the MFMA dequant-GEMM (M >= 5). Accumulation is fp32; the
+ * GEMM rounds each decoded RTN weight s q to fp16 (the zero-point term s z
+ * sum_k x'_k is added separately). The RTN GEMM needs N*K*b/8 < 2^31 - 4096
+ * (LBQ_ERR_SHAPE otherwise). The result of a call does not depend on timing:
+ * repeat calls give identical bits. */
 lbq_status lbq_linear_forward(const lbq_weight *w, const uint16_t *x, int32_t M,
                               uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 

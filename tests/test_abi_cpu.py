@@ -68,6 +68,23 @@ def test_host_pack_is_byte_identical_to_oracle(L, bits, n, k):
     assert np.array_equal(meta, om.view(np.uint8).reshape(-1))
 
 
+def test_pack_rejects_rtn_scales_from_128(L):
+    """The MFMA GEMM decodes with the fp16 constants -64 s and -16 s z, so the
+    packer refuses RTN groups whose scale reaches 128 and keeps everything
+    below (weights scaled by 2000 give scales near 80)."""
+    s = synth.signs(256, workload=8, item=7)
+    w = synth.weights(4, 256, workload=8, item=7)
+    for bits in (2, 4):
+        _, meta = L.pack(w * 2000.0, bits, s)
+        sc = np.frombuffer(meta.tobytes(), dtype=np.float16)[0::2].astype(np.float64)
+        assert sc.max() < 128
+    _, meta = L.pack(w * 2000.0, 2, s)
+    assert np.frombuffer(meta.tobytes(), dtype=np.float16)[0::2].astype(np.float64).max() > 40
+    with pytest.raises(L.LbqError) as e:
+        L.pack(w * 8000.0, 2, s)
+    assert e.value.status == -6
+
+
 def test_host_pack_full_single_linear(L):
     w = synth.weights(4096, 4096, workload=synth.W_SINGLE)
     s = synth.signs(4096, workload=synth.W_SINGLE)

@@ -212,23 +212,40 @@ def test_zero_tokens_is_noop(L, dev):
 
 
 def test_zero_weights_give_zero_output(L, dev):
-    """All-zero weights pack to codes 0 with the degenerate scale 1. Both paths
-    insert codes into fp16 constants (1.0 in the GEMV, 2^(10-m) in the GEMM)
-    and remove them again with per-group activation sums, so they leave an
-    fp32 cancellation residue of a few ulps of those sums. With |x| ~ 1 the
-    GEMM's sums reach ~4e3 (ulp 2.4e-4 at 4096), the GEMV's per-class ones far
-    less; a wrong offset or zero point would leave residues of order 1 or more."""
+    """All-zero weights pack to codes 0 with the degenerate scale 1. The GEMM
+    decodes round(s q) = 0 and a zero-point term of 0, so it returns exact
+    zeros. The GEMV inserts codes into fp16 1.0 and removes the offsets with
+    per-class activation sums, which leaves an fp32 cancellation residue of a
+    few ulps of those sums; a wrong offset or zero point would leave residues
+    of order 1 or more."""
     from bit_weight_only_amd import lbq
 
     k, n = 256, 32
     s = synth.signs(k, workload=15)
     planes, meta = lbq.pack(np.zeros((n, k), np.float32), 2, s)
     pl = lbq.PackedLinear.from_host(planes, meta, s, k, n, 2)
-    x = to_dev(synth.activations(3, k, workload=15), dev)
+    x = to_dev(synth.activations(5, k, workload=15), dev)
     y = L.linear_forward(pl, x, path=L.PATH_GEMM).cpu().numpy().astype(np.float64)
-    assert np.abs(y).max() < 1e-2
-    y = L.linear_forward(pl, x, path=L.PATH_GEMV).cpu().numpy().astype(np.float64)
+    assert np.abs(y).max() == 0.0
+    y = L.linear_forward(pl, x[:3], path=L.PATH_GEMV).cpu().numpy().astype(np.float64)
     assert np.abs(y).max() < 2e-3
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("m", [3, 40])
+def test_large_scales_stay_finite(L, dev, bits, m):
+    """Weights 2000 times the usual size give group scales near the packer's
+    limit of 128 (2-bit) and code-weighted zero terms near the top of the fp16
+    constants the GEMM decodes with; both paths stay within tolerance."""
+    n, k = 96, 1024
+    w = synth.weights(n, k, workload=15, item=40 + bits) * 2000.0
+    s = synth.signs(k, workload=15, item=40 + bits)
+    planes, meta = L.pack(w, bits, s)
+    pl = L.PackedLinear.from_host(planes, meta, s, k, n, bits)
+    x = synth.activations(m, k, workload=15, item=m)
+    y = L.linear_forward(pl, to_dev(x, dev)).cpu().numpy().astype(np.float64)
+    assert np.isfinite(y).all()
+    assert O.rel_l2(y, oracle_rtn_rows(w, s, bits, x)) < TOL
 
 
 # ---------------------------------------------------------------- product-VQ
