@@ -120,6 +120,76 @@ __device__ __forceinline__ void row_partial(const uint4 *__restrict__ prow, cons
   }
 }
 
+// U rows at once: the loads of all U rows' planes and (scale, zero) words for a
+// group are issued before any of them is decoded, so U memory round trips
+// overlap; the staged activations of a slot are read once for all U rows.
+// prow[u] / mrow[u] as in row_partial; adds into yacc[u][MT].
+template <int BITS, int MT, int L, int U>
+__device__ __forceinline__ void rows_partial(const uint4 *const *prow, const uint32_t *const *mrow,
+                                             const uint32_t *xx, const float2 *sums, int Gc, int gn, int j,
+                                             float (&yacc)[U][MT]) {
+  constexpr int NC = num_classes<BITS>();
+  for (int g = j; g < gn; g += L) {
+    uint4 pv[U][BITS];
+    uint32_t mw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) pv[u][p] = prow[u][g * BITS + p];
+      mw[u] = mrow[u][g];
+    }
+    float acc[U][MT][NC];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t h[U][16];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        uint32_t pw[BITS];
+#pragma unroll
+        for (int p = 0; p < BITS; ++p)
+          pw[p] = (w == 0) ? pv[u][p].x : (w == 1) ? pv[u][p].y : (w == 2) ? pv[u][p].z : pv[u][p].w;
+        if constexpr (BITS == 2) decode_slots2(pw[0], pw[1], h[u]);
+        else decode_slots_nib<BITS>(pw, h[u]);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const uint4 *xs = reinterpret_cast<const uint4 *>(xx + (m * Gc + g) * kGroupStride + w * 16);
+        uint32_t xv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = xs[i];
+          xv[4 * i] = v.x;
+          xv[4 * i + 1] = v.y;
+          xv[4 * i + 2] = v.z;
+          xv[4 * i + 3] = v.w;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const int cls = slot_class<BITS>(c);
+            acc[u][m][cls] =
+                dot2(h[u][c], xv[c], (w == 0 && c == first_slot_of_class<BITS>(cls)) ? 0.f : acc[u][m][cls]);
+          }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float sc = f16_bits_to_f32(mw[u] & 0xFFFFu);
+      const float zp = f16_bits_to_f32(mw[u] >> 16);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float2 pt = sums[m * Gc + g];
+        float t = -pt.x;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) t = fmaf(class_weight<BITS>(c), acc[u][m][c], t);
+        t = fmaf(-zp, pt.y, t);
+        yacc[u][m] = fmaf(sc, t, yacc[u][m]);
+      }
+    }
+  }
+}
+
 // Sum per-lane partials over the L lanes that share a row (aligned clusters).
 template <int MT, int L>
 __device__ __forceinline__ void reduce_cluster(float yacc[MT]) {

@@ -6,7 +6,8 @@
 //   1. route:   one workgroup; per token (a wavefront each) the top_k logits
 //               (ties to the lower expert id) and softmax weights over them;
 //               per-expert counts, exclusive offsets, and the assignment list
-//               grouped by expert.
+//               grouped by expert (a counting sort over token chunks, one
+//               wavefront per chunk).
 //   2. rotate:  x' = R_hidden x once per token (the rotate kernel).
 //   3. gate|up: one workgroup per (expert, 128-wide block of the ffn axis);
 //               inactive experts exit at once. It decodes the 128 gate rows and
@@ -61,11 +62,10 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
                                                                   int32_t *__restrict__ counts,
                                                                   int32_t *__restrict__ offsets,
                                                                   int32_t *__restrict__ perm) {
-  __shared__ int32_t s_ids[kMaxAssignments];
-  __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_cur[kMaxExperts];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kWaves = kRouteThreads / 64;
+  __shared__ int32_t s_ids[kMaxAssignments];
+  __shared__ int32_t s_cnt[kWaves * kMaxExperts];   // per (token chunk, expert): count, then run start
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   // 1. top-k per token, one wavefront per token. Expert e = lane + 64 i is the
   //    key (order(logit) << 32 | kMaxExperts - 1 - e): the largest key is the
@@ -113,16 +113,23 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
     denom = add_xor<1>(denom);
     if (lane < top_k) weights[t * top_k + lane] = ex / denom;
   }
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) s_cnt[e] = 0;
-  __syncthreads();
+  // 2. counting sort of the assignments by expert, stable in the assignment
+  //    index. Wave w owns the contiguous token chunk [w C, (w + 1) C); a
+  //    token's top_k experts are distinct, so the lanes of one token never
+  //    touch the same counter. (a) per-chunk counts cnt[w][e]; (b) per expert
+  //    the total and, after an exclusive scan over experts, the start of each
+  //    chunk's run; (c) each wave walks its tokens in order and places them.
   const int MK = M * top_k;
-  for (int a = threadIdx.x; a < MK; a += kRouteThreads) {
-    ids[a] = s_ids[a];
-    atomicAdd(&s_cnt[s_ids[a]], 1);
-  }
+  const int chunk = (M + kWaves - 1) / kWaves;
+  const int t_lo = min(M, wave * chunk), t_hi = min(M, t_lo + chunk);
+  for (int i = threadIdx.x; i < kWaves * E; i += kRouteThreads) s_cnt[i] = 0;
   __syncthreads();
-  // 2. exclusive offsets: thread i owns experts kPerThread i .. kPerThread (i + 1) - 1;
-  //    scan of the per-thread totals within each wave, then across the waves
+  for (int a = threadIdx.x; a < MK; a += kRouteThreads) ids[a] = s_ids[a];
+  for (int t = t_lo; t < t_hi; ++t)
+    if (lane < top_k) s_cnt[wave * E + s_ids[t * top_k + lane]] += 1;
+  __syncthreads();
+  // exclusive offsets: thread i owns experts kPerThread i .. kPerThread (i + 1) - 1;
+  // scan of the per-thread totals within each wave, then across the waves
   {
     constexpr int kPerThread = (kMaxExperts + kRouteThreads - 1) / kRouteThreads;
     __shared__ int32_t s_wave[kWaves];
@@ -131,8 +138,11 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int e = threadIdx.x * kPerThread + j;
-      own[j] = e < E ? s_cnt[e] : 0;
-      sum += own[j];
+      int tot = 0;
+      if (e < E)
+        for (int w = 0; w < kWaves; ++w) tot += s_cnt[w * E + e];
+      own[j] = tot;
+      sum += tot;
     }
     int incl = sum;
 #pragma unroll
@@ -149,37 +159,25 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
       const int e = threadIdx.x * kPerThread + j;
       if (e < E) {
         offsets[e] = run;
-        s_cur[e] = run;
         counts[e] = own[j];
+        // start of each chunk's run of expert e
+        int pos = run;
+        for (int w = 0; w < kWaves; ++w) {
+          const int c = s_cnt[w * E + e];
+          s_cnt[w * E + e] = pos;
+          pos += c;
+        }
       }
       run += own[j];
     }
     if (threadIdx.x == kRouteThreads - 1) offsets[E] = run;
   }
   __syncthreads();
-  // 3. assignment list grouped by expert, increasing assignment index within an
-  //    expert: wavefront 0 walks the assignments in chunks of 64; lane l's rank
-  //    among the chunk's earlier lanes with the same expert comes from a scan
-  //    of the chunk's expert ids, and the expert's last lane in the chunk moves
-  //    its write position past the chunk's entries.
-  if (wave == 0) {
-    for (int c0 = 0; c0 < MK; c0 += 64) {
-      const int a = c0 + lane;
-      const int e = a < MK ? s_ids[a] : -1;
-      const int n = __builtin_amdgcn_readfirstlane(min(64, MK - c0));
-      int rank = 0, cnt = 0;
-      for (int jj = 0; jj < n; ++jj) {
-        const int same = __builtin_amdgcn_readlane(e, jj) == e;
-        rank += (jj < lane) & same;
-        cnt += same;
-      }
-      if (a < MK) {
-        const int base = s_cur[e];
-        perm[base + rank] = a;
-        if (rank == cnt - 1) s_cur[e] = base + cnt;
-      }
+  for (int t = t_lo; t < t_hi; ++t)
+    if (lane < top_k) {
+      const int a = t * top_k + lane;
+      perm[s_cnt[wave * E + s_ids[a]]++] = a;
     }
-  }
 }
 
 // ------------------------------------------------------------------ gate|up
@@ -205,18 +203,33 @@ __device__ void gateup_tile(const MoeArgs &a, int e, int ib, int first, int cnt,
   const uint4 *planes = reinterpret_cast<const uint4 *>(a.planes + a.gu_plane_off[e]);
   const uint32_t *meta = reinterpret_cast<const uint32_t *>(a.meta + a.gu_meta_off[e]);
   const int j = threadIdx.x % L;
-  for (int p = 0; p < (2 * kGuRows) / R; ++p) {
-    const int local = p * R + threadIdx.x / L;                 // 0..255: gate rows then up rows
-    const int row = (local < kGuRows) ? (ib * kGuRows + local) : (a.ffn + ib * kGuRows + local - kGuRows);
-    float yacc[MT];
+  // U passes of R rows at once (their loads in flight together)
+  constexpr int U = MT <= 2 ? 4 : MT <= 4 ? 2 : 1;
+  for (int p = 0; p < (2 * kGuRows) / R; p += U) {
+    const uint4 *prow[U];
+    const uint32_t *mrow[U];
+    int local[U];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) yacc[m] = 0.f;
-    row_partial<BITS, MT, L>(planes + static_cast<size_t>(row) * G * BITS, meta + static_cast<size_t>(row) * G, xx,
-                             sums, Gc, G, j, yacc);
-    reduce_cluster<MT, L>(yacc);
-    if (j == 0) {
+    for (int u = 0; u < U; ++u) {
+      local[u] = (p + u) * R + threadIdx.x / L;                 // 0..255: gate rows then up rows
+      const int row =
+          (local[u] < kGuRows) ? (ib * kGuRows + local[u]) : (a.ffn + ib * kGuRows + local[u] - kGuRows);
+      prow[u] = planes + static_cast<size_t>(row) * G * BITS;
+      mrow[u] = meta + static_cast<size_t>(row) * G;
+    }
+    float yacc[U][MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) hbuf[local * MT + m] = yacc[m];
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) yacc[u][m] = 0.f;
+    rows_partial<BITS, MT, L, U>(prow, mrow, xx, sums, Gc, G, j, yacc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      reduce_cluster<MT, L>(yacc[u]);
+      if (j == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) hbuf[local[u] * MT + m] = yacc[u][m];
+      }
     }
   }
   __syncthreads();
@@ -286,18 +299,32 @@ __device__ void down_tile(const MoeArgs &a, int e, int rb, int first, int cnt, u
   const uint4 *planes = reinterpret_cast<const uint4 *>(a.planes + a.dn_plane_off[e]);
   const uint32_t *meta = reinterpret_cast<const uint32_t *>(a.meta + a.dn_meta_off[e]);
   const int j = threadIdx.x % L;
-  for (int p = 0; p < kDnRows / R; ++p) {
-    const int row = rb * kDnRows + p * R + threadIdx.x / L;
-    float yacc[MT];
+  // U passes of R rows at once (their loads in flight together)
+  constexpr int U = MT <= 2 ? 4 : MT <= 4 ? 2 : 1;
+  for (int p = 0; p < kDnRows / R; p += U) {
+    const uint4 *prow[U];
+    const uint32_t *mrow[U];
+    int row[U];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) yacc[m] = 0.f;
-    row_partial<BITS, MT, L>(planes + static_cast<size_t>(row) * G * BITS, meta + static_cast<size_t>(row) * G, xx,
-                             sums, Gc, G, j, yacc);
-    reduce_cluster<MT, L>(yacc);
-    if (j == 0) {
+    for (int u = 0; u < U; ++u) {
+      row[u] = rb * kDnRows + (p + u) * R + threadIdx.x / L;
+      prow[u] = planes + static_cast<size_t>(row[u]) * G * BITS;
+      mrow[u] = meta + static_cast<size_t>(row[u]) * G;
+    }
+    float yacc[U][MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < cnt) a.out[static_cast<size_t>(perm[m]) * a.hidden + row] = yacc[m];
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) yacc[u][m] = 0.f;
+    rows_partial<BITS, MT, L, U>(prow, mrow, xx, sums, Gc, G, j, yacc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      reduce_cluster<MT, L>(yacc[u]);
+      if (j == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < cnt) a.out[static_cast<size_t>(perm[m]) * a.hidden + row[u]] = yacc[u][m];
+      }
     }
   }
   __syncthreads();
