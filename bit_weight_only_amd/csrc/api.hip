@@ -205,7 +205,7 @@ lbq_status lbq_rotate(const uint16_t *x, int32_t M, int32_t K, const int8_t *sig
 namespace {
 
 struct MoeLayout {
-  size_t xr, ids, weights, counts, offsets, perm, act, out, total;
+  size_t xr, ids, weights, counts, offsets, perm, act, out, h, total;
 };
 
 MoeLayout moe_layout(const lbq_moe *m, int M) {
@@ -225,6 +225,7 @@ MoeLayout moe_layout(const lbq_moe *m, int M) {
   L.perm = take(mk * 4);
   L.act = take(mk * m->ffn * 2);
   L.out = take(mk * m->hidden * 4);
+  L.h = take(mk * m->ffn * 2 * 4);
   L.total = off;
   return L;
 }
@@ -278,9 +279,11 @@ lbq_status lbq_moe_forward(const lbq_moe *m, const uint16_t *x, const float *log
   a.dn_meta_off = m->dn_meta_off;
   a.planes = static_cast<const uint8_t *>(m->planes);
   a.meta = static_cast<const uint8_t *>(m->meta);
+  a.signs_hidden = m->signs_hidden;
   a.signs_ffn = m->signs_ffn;
-  uint16_t *xr = reinterpret_cast<uint16_t *>(base + L.xr);
-  a.xr = xr;
+  a.x = x;
+  a.xr = reinterpret_cast<uint16_t *>(base + L.xr);
+  a.h = reinterpret_cast<float *>(base + L.h);
   int32_t *ids = reinterpret_cast<int32_t *>(base + L.ids);
   float *wts = reinterpret_cast<float *>(base + L.weights);
   int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
@@ -294,7 +297,6 @@ lbq_status lbq_moe_forward(const lbq_moe *m, const uint16_t *x, const float *log
   a.y = y;
   if (launch_moe_route(logits, M, m->E, m->top_k, ids, wts, counts, offsets, perm, s) != hipSuccess)
     return LBQ_ERR_HIP;
-  if (launch_rotate(x, M, m->hidden, m->signs_hidden, xr, s) != hipSuccess) return LBQ_ERR_HIP;
   return hip_status(launch_moe_experts(a, s));
 }
 

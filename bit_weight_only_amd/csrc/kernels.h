@@ -79,16 +79,22 @@ struct MoeArgs {
   const uint8_t *bits;
   const uint64_t *gu_plane_off, *gu_meta_off, *dn_plane_off, *dn_meta_off;
   const uint8_t *planes, *meta;
-  const int8_t *signs_ffn;
-  const uint16_t *xr;        // [M][hidden] rotated tokens
+  const int8_t *signs_hidden, *signs_ffn;
+  const uint16_t *x;         // [M][hidden] tokens
+  const uint16_t *xr;        // [M][hidden] rotated tokens (VALU expert kernels)
+  float *h;                  // [M*top_k][2*ffn] gate|up results (matrix-core expert kernels)
   const int32_t *offsets;    // [E+1]
   const int32_t *perm;       // [M*top_k]
   const float *weights;      // [M][top_k]
-  uint16_t *act;             // [M*top_k][ffn] rotated SwiGLU output, by assignment index
+  uint16_t *act;             // [M*top_k][ffn] SwiGLU output by assignment index (rotated for the VALU kernels)
   float *out;                // [M*top_k][hidden] expert outputs, by assignment index
   uint16_t *y;               // [M][hidden]
 };
+// Rotation (VALU path), expert linears and the weighted combine.
 hipError_t launch_moe_experts(const MoeArgs &a, hipStream_t s);
+// Expert linears on the matrix cores (gate|up, SwiGLU, down; rotations fused).
+bool moe_mx_supported(int hidden, int ffn, const int8_t *signs_hidden, const int8_t *signs_ffn);
+hipError_t launch_moe_mx(const MoeArgs &a, hipStream_t s);
 // Dynamic LDS the expert kernels need (must stay within 64 KB).
 size_t moe_gateup_lds(int hidden);
 size_t moe_down_lds(int ffn);

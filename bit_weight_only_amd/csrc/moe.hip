@@ -388,12 +388,17 @@ size_t moe_down_lds(int ffn) { return static_cast<size_t>(kMaxTokChunk) * (ffn /
 
 hipError_t launch_moe_experts(const MoeArgs &a, hipStream_t s) {
   hipError_t e;
-  hipLaunchKernelGGL(moe_gateup_kernel, dim3(a.E * (a.ffn / kGuRows)), dim3(kGemvThreads), moe_gateup_lds(a.hidden),
-                     s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_down_kernel, dim3(a.E * (a.hidden / kDnRows)), dim3(kGemvThreads), moe_down_lds(a.ffn), s,
-                     a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (moe_mx_supported(a.hidden, a.ffn, a.signs_hidden, a.signs_ffn)) {
+    if ((e = launch_moe_mx(a, s)) != hipSuccess) return e;
+  } else {
+    if ((e = launch_rotate(a.x, a.M, a.hidden, a.signs_hidden, const_cast<uint16_t *>(a.xr), s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(moe_gateup_kernel, dim3(a.E * (a.ffn / kGuRows)), dim3(kGemvThreads), moe_gateup_lds(a.hidden),
+                       s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(moe_down_kernel, dim3(a.E * (a.hidden / kDnRows)), dim3(kGemvThreads), moe_down_lds(a.ffn), s,
+                       a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const long total = static_cast<long>(a.M) * a.hidden;
   hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, a.out,
                      a.weights, a.M, a.hidden, a.top_k, a.y);

@@ -73,7 +73,10 @@ def _oracle_expert(w_gu, w_dn, bits, sh, sf, hidden, ffn):
     return get
 
 
-@pytest.mark.parametrize("m,E,hidden,ffn,top_k", [(5, 8, 256, 128, 2), (1, 4, 384, 256, 4), (19, 16, 512, 256, 3)])
+# hidden and ffn multiples of 512 (with 16-byte aligned signs) run the
+# matrix-core expert kernels; the others the VALU expert kernels
+@pytest.mark.parametrize("m,E,hidden,ffn,top_k", [(5, 8, 256, 128, 2), (1, 4, 384, 256, 4), (19, 16, 512, 256, 3),
+                                                  (3, 8, 512, 512, 2), (13, 16, 1024, 512, 4), (1, 8, 2048, 1024, 8)])
 def test_moe_small_blocks(L, dev, m, E, hidden, ffn, top_k):
     say(f"moe small m={m} E={E} hidden={hidden} ffn={ffn} k={top_k}")
     bits = synth.expert_bits(E, workload=17, item=E)
@@ -87,10 +90,11 @@ def test_moe_small_blocks(L, dev, m, E, hidden, ffn, top_k):
     assert e < TOL
 
 
-def test_moe_every_width_and_crowded_expert(L, dev):
-    """All tokens pick the same experts (more than one token chunk per expert)
-    and each width appears."""
-    E, hidden, ffn, top_k, m = 6, 256, 128, 3, 21
+@pytest.mark.parametrize("hidden,ffn", [(256, 128), (512, 512)], ids=["valu", "matrix_core"])
+def test_moe_every_width_and_crowded_expert(L, dev, hidden, ffn):
+    """All tokens pick the same experts (more than one token chunk per expert:
+    8 on the VALU kernels, 4 on the matrix cores) and each width appears."""
+    E, top_k, m = 6, 3, 21
     bits = np.array([2, 3, 4, 2, 3, 4], np.uint8)
     sh, sf, w_gu, w_dn, moe = _block(L, E, hidden, ffn, top_k, bits, 18)
     x = synth.activations(m, hidden, workload=18)
@@ -99,6 +103,17 @@ def test_moe_every_width_and_crowded_expert(L, dev):
     y = L.moe_forward(moe, to_dev(x, dev), to_dev(lg, dev)).cpu().numpy().astype(np.float64)
     want = O.moe_forward(x, lg, top_k, _oracle_expert(w_gu, w_dn, bits, sh, sf, hidden, ffn))
     assert O.rel_l2(y, want) < TOL
+
+
+def test_moe_repeat_calls_bit_identical(L, dev):
+    E, hidden, ffn, top_k, m = 16, 512, 512, 4, 13
+    bits = synth.expert_bits(E, workload=19, item=E)
+    sh, sf, w_gu, w_dn, moe = _block(L, E, hidden, ffn, top_k, bits, 19)
+    x = to_dev(synth.activations(m, hidden, workload=19), dev)
+    lg = to_dev(synth.logits(m, E, workload=19), dev)
+    a = L.moe_forward(moe, x, lg).cpu().numpy()
+    b = L.moe_forward(moe, x, lg).cpu().numpy()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
 def test_moe_block_full_size_sampled_tokens(L, dev):
