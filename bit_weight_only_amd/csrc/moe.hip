@@ -43,15 +43,28 @@ __device__ __forceinline__ float float_unorder(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 template <int X>
-__device__ __forceinline__ uint64_t max_with_xor_u64(uint64_t v) {
-  const uint32_t lo = xor_lane_u32<X>(static_cast<uint32_t>(v));
-  const uint32_t hi = xor_lane_u32<X>(static_cast<uint32_t>(v >> 32));
-  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-  return o > v ? o : v;
-}
-template <int X>
 __device__ __forceinline__ float add_xor(float v) {
   return v + __uint_as_float(xor_lane_u32<X>(__float_as_uint(v)));
+}
+
+// Largest u32 over the wavefront, in every lane (uniform): a DPP max
+// reduction into lane 63 (row shifts by 1, 2, 4, 8 give each row's maximum
+// in its lane 15; row broadcasts 15 and 31 carry them to lane 63), then a
+// read of lane 63. Lanes without a DPP source keep their own value.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
+  const uint32_t o = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, ROWS, 0xF, false));
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max_dpp<0x111, 0xF>(v);   // row_shr:1
+  v = max_dpp<0x112, 0xF>(v);   // row_shr:2
+  v = max_dpp<0x114, 0xF>(v);   // row_shr:4
+  v = max_dpp<0x118, 0xF>(v);   // row_shr:8
+  v = max_dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = max_dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
 // PER: experts per lane (E <= 64 PER).
@@ -67,51 +80,69 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
   __shared__ int32_t s_cnt[kWaves * kMaxExperts];   // per (token chunk, expert): count, then run start
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // 1. top-k per token, one wavefront per token. Expert e = lane + 64 i is the
-  //    key (order(logit) << 32 | kMaxExperts - 1 - e): the largest key is the
-  //    largest logit, ties to the lower id; a selected key is cleared to 0.
-  for (int t = wave; t < M; t += kWaves) {
+  // 1. top-k per token, one wavefront per pair of tokens (their dependent
+  //    chains interleave). Expert e = lane + 64 i holds the order key of its
+  //    logit (order-preserving u32; a selected or absent expert holds 0, below
+  //    every finite logit's key). Each round takes the wavefront's largest key
+  //    and, among the experts holding it, the lowest id (ties go to the lower
+  //    id), and clears it. A pair's second token past M computes on copies of
+  //    the first and stores nothing.
+  for (int t0 = 2 * wave; t0 < M; t0 += 2 * kWaves) {
+    const int tt[2] = {t0, min(t0 + 1, M - 1)};
+    const bool ok1 = t0 + 1 < M;
     // all loads first, unconditionally at clamped indices, then the keys
-    float lv[PER];
+    float lv[2][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) lv[i] = logits[static_cast<size_t>(t) * E + min(lane + 64 * i, E - 1)];
-    uint64_t key[PER];
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane + 64 * i;
-      key[i] = e < E ? (static_cast<uint64_t>(float_order(lv[i])) << 32) | static_cast<uint32_t>(kMaxExperts - 1 - e)
-                     : 0;
-    }
+      for (int i = 0; i < PER; ++i) lv[p][i] = logits[static_cast<size_t>(tt[p]) * E + min(lane + 64 * i, E - 1)];
+    uint32_t key[2][PER];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) key[p][i] = lane + 64 * i < E ? float_order(lv[p][i] + 0.0f) : 0u;   // -0 -> +0
     // lane r keeps the r-th selected logit (selection order is descending)
-    float sel0 = 0.f, mine = 0.f;
+    float sel0[2] = {0.f, 0.f}, mine[2] = {0.f, 0.f};
     for (int r = 0; r < top_k; ++r) {
-      uint64_t best = 0;
+      uint32_t best[2];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) best = key[i] > best ? key[i] : best;
-      best = max_with_xor_u64<32>(best);
-      best = max_with_xor_u64<16>(best);
-      best = max_with_xor_u64<8>(best);
-      best = max_with_xor_u64<4>(best);
-      best = max_with_xor_u64<2>(best);
-      best = max_with_xor_u64<1>(best);
-      const int e = kMaxExperts - 1 - static_cast<int>(static_cast<uint32_t>(best));
-      const float v = float_unorder(static_cast<uint32_t>(best >> 32));
+      for (int p = 0; p < 2; ++p) {
+        uint32_t m = key[p][0];
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (i == (e >> 6) && lane == (e & 63)) key[i] = 0;
-      if (r == 0) sel0 = v;
-      if (lane == r) mine = v;
-      if (lane == 0) s_ids[t * top_k + r] = e;
+        for (int i = 1; i < PER; ++i) m = key[p][i] > m ? key[p][i] : m;
+        best[p] = m;
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) best[p] = wave_max_u32(best[p]);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        int e = 64 * PER;
+#pragma unroll
+        for (int i = PER - 1; i >= 0; --i) {
+          const uint64_t bal = __ballot(key[p][i] == best[p]);
+          if (bal) e = 64 * i + __builtin_ctzll(bal);
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (i == (e >> 6) && lane == (e & 63)) key[p][i] = 0u;
+        const float v = float_unorder(best[p]);
+        if (r == 0) sel0[p] = v;
+        if (lane == r) mine[p] = v;
+        if (lane == 0 && (p == 0 || ok1)) s_ids[tt[p] * top_k + r] = e;
+      }
     }
     // softmax over the selected logits (shifted by the largest)
-    const float ex = lane < top_k ? __expf(mine - sel0) : 0.f;
-    float denom = add_xor<32>(ex);
-    denom = add_xor<16>(denom);
-    denom = add_xor<8>(denom);
-    denom = add_xor<4>(denom);
-    denom = add_xor<2>(denom);
-    denom = add_xor<1>(denom);
-    if (lane < top_k) weights[t * top_k + lane] = ex / denom;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float ex = lane < top_k ? __expf(mine[p] - sel0[p]) : 0.f;
+      float denom = add_xor<32>(ex);
+      denom = add_xor<16>(denom);
+      denom = add_xor<8>(denom);
+      denom = add_xor<4>(denom);
+      denom = add_xor<2>(denom);
+      denom = add_xor<1>(denom);
+      if (lane < top_k && (p == 0 || ok1)) weights[tt[p] * top_k + lane] = ex / denom;
+    }
   }
   // 2. counting sort of the assignments by expert, stable in the assignment
   //    index. Wave w owns the contiguous token chunk [w C, (w + 1) C); a
