@@ -57,7 +57,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 DOMINANT = "gemv_mfma_kernel"
 # sources the dominant kernel is built from (traffic from counters is stale once they change)
-DOMINANT_SOURCES = ["bit_weight_only_amd/csrc/gemv_mfma.hip", "bit_weight_only_amd/csrc/device.h"]
+DOMINANT_SOURCES = ["bit_weight_only_amd/csrc/gemv_mfma.hip", "bit_weight_only_amd/csrc/mx_core.h",
+                    "bit_weight_only_amd/csrc/gemm_common.h", "bit_weight_only_amd/csrc/device.h"]
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "gemv_mfma_dense_stack_m1.txt")
 CALIB_BYTES = 512 << 20        # the copy kernel reads and writes this many bytes
 
