@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblbq.so")
 
-HIP_SOURCES = ["api.hip", "rotate.hip", "gemv.hip", "gemv_fold.hip", "gemv_mfma.hip", "gemm.hip", "gemm_rtn.hip", "pvq.hip", "moe.hip", "moe_mx.hip", "unpack.hip"]
+HIP_SOURCES = ["api.hip", "rotate.hip", "gemv.hip", "gemv_fold.hip", "gemv_mfma.hip", "gemm.hip", "gemm_rtn.hip", "pvq.hip", "pvq_mx.hip", "moe.hip", "moe_mx.hip", "unpack.hip"]
 HOST_SOURCES = ["pack.cpp"]
 
 ARCH = os.environ.get("LBQ_OFFLOAD_ARCH", "gfx950")

@@ -66,6 +66,14 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
   if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_mfma_supported(M, w->K, w->N) && aligned16(w->signs))
     return hip_status(launch_gemv_mfma(w->planes, w->meta, x, w->signs, y, M, w->K, w->N, w->bits, 0, 0, 0, s, ev0,
                                        ev1));
+  if (w->format == LBQ_FMT_PVQ_4x8 && gemv && gemv_pvq_mx_supported(M, w->K, w->N) && aligned16(w->signs) &&
+      (reinterpret_cast<uintptr_t>(w->codebook) & 3u) == 0) {
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return LBQ_ERR_HIP;
+    if (launch_gemv_pvq_mx(static_cast<const uint8_t *>(w->planes), static_cast<const uint16_t *>(w->meta),
+                           static_cast<const uint8_t *>(w->codebook), x, w->signs, y, M, w->K, w->N, s) != hipSuccess)
+      return LBQ_ERR_HIP;
+    return (ev1 && hipEventRecord(ev1, s) != hipSuccess) ? LBQ_ERR_HIP : LBQ_OK;
+  }
   uint16_t *xr = static_cast<uint16_t *>(ws);
   if (!gemv) {
     // MFMA GEMM: rotation into the folded order (with the RTN zero-point sums,

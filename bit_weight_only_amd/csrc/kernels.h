@@ -46,6 +46,14 @@ hipError_t launch_gemv_mfma(const void *planes, const void *meta, const uint16_t
 // Product-VQ GEMV (M <= 16) on rotated activations.
 hipError_t launch_gemv_pvq(const uint8_t *idx, const uint16_t *scale, const uint8_t *codebook, const uint16_t *xr,
                            uint16_t *y, int M, int K, int N, hipStream_t s);
+// Product-VQ GEMV on raw activations x [M][K] (1 <= M <= 4) on the matrix
+// cores (fp8 activation pieces x fp8 codebook values), rotation fused into the
+// prologue: one launch, no workspace. x and signs 16-byte aligned, codebook
+// 4-byte aligned.
+bool gemv_pvq_mx_supported(int M, int K, int N);
+hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, const uint8_t *codebook,
+                              const uint16_t *x, const int8_t *signs, uint16_t *y, int M, int K, int N,
+                              hipStream_t s);
 // MFMA dequant-GEMMs on activations rotated into the folded slot order
 // (launch_rotate_folded): RTN planes (gemm_rtn_plan, launch_gemm_rtn, with the
 // rotation's tz sums) and product-VQ (gemm_plan, launch_gemm_pvq). A plan fixes

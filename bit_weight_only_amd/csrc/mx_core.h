@@ -133,25 +133,30 @@ __device__ __forceinline__ RotIn rot_load(__amdgpu_buffer_rsrc_t xrs, __amdgpu_b
   return r;
 }
 
-// Rotate one unit and split it into the A pieces, (H_128 D x)_g with the
-// 1/sqrt(128) normalisation folded into the piece scale.
+// Rotation of one unit: the 16 values of lane L, (H_128 D x) at positions
+// 16 L .. 16 L + 15 of the group, up to a sign, with the 1/sqrt(128)
+// normalisation and the group's power-of-two scale folded into c: v[i] * c is
+// the scaled rotated value (largest magnitude of the group in [128, 256)).
 //  * Cross-lane stages first, on the signed inputs, each one v_fmac with a DPP
 //    operand: v += sg * partner with sg = -1 on the lane whose bit is set.
 //    That lane gets v - partner, the negated butterfly output; the pair
 //    partners always carry the same accumulated sign, so after the three
 //    stages lane L holds (-1)^popcount(L) times the exact value, and the
-//    factor goes into the lane's piece scale.
+//    factor goes into c.
 //  * Four in-lane stages.
-//  * Positions 16 L + s + 4 e (e = 0..3) form one 4-byte word of the A layout
-//    (see the file comment): four words per piece per lane.
-// Sylvester's H_128 has column sums 128, 0, 0, ..., so the group sum is
-// T_g = sqrt(128) s_0 x_0 (exact, no reduction). ss[t * Gp + g] = (2 / sc_g,
-// T_g). store = false computes without writing.
-__device__ __forceinline__ void rot_pieces(const RotIn &in, int Gp, int m, int g, int L, bool store, uint32_t *xa,
-                                           float2 *ss) {
+// E is the group's exponent (max |x'| = f 2^E, f in [0.5, 1); scale 2^(8 - E)).
+// first = s_0 x_0 on lane 0: Sylvester's H_128 has column sums 128, 0, 0, ...,
+// so the group sum is T_g = sqrt(128) s_0 x_0 (exact, no reduction).
+struct RotUnit {
+  float v[16];
+  float c, first;
+  int E;
+};
+__device__ __forceinline__ RotUnit rot_unit(const RotIn &in, int L) {
+  RotUnit u;
+  float *v = u.v;
   const uint32_t xw[8] = {in.xa.x, in.xa.y, in.xa.z, in.xa.w, in.xb.x, in.xb.y, in.xb.z, in.xb.w};
   const uint32_t sw[4] = {in.sv.x, in.sv.y, in.sv.z, in.sv.w};
-  float v[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t sb = sw[i >> 1] >> (16 * (i & 1));   // sign bytes of elements 2i, 2i + 1
@@ -159,7 +164,7 @@ __device__ __forceinline__ void rot_pieces(const RotIn &in, int Gp, int m, int g
     v[2 * i] = half_lo(h);
     v[2 * i + 1] = half_hi(h);
   }
-  const float first = v[0];   // s_0 x_0 on lane 0
+  u.first = v[0];   // s_0 x_0 on lane 0
   {
     const float sg = (L & 1) ? -1.f : 1.f;
 #pragma unroll
@@ -192,34 +197,53 @@ __device__ __forceinline__ void rot_pieces(const RotIn &in, int Gp, int m, int g
   mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
   mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
   mx = fmaxf(mx, dpp_f<kDppXor8>(mx));
-  // sc = 2^(8 - E) with max |x'| = f 2^E, f in [0.5, 1): scaled maximum in [128, 256)
-  const int E = __builtin_amdgcn_frexp_expf(mx * kInvSqrt128);
+  u.E = __builtin_amdgcn_frexp_expf(mx * kInvSqrt128);
   const float flip = (__builtin_popcount(L) & 1) ? -1.f : 1.f;
-  const float c = __builtin_amdgcn_ldexpf(flip * kInvSqrt128, 8 - E);
+  u.c = __builtin_amdgcn_ldexpf(flip * kInvSqrt128, 8 - u.E);
+  return u;
+}
+
+// Three e4m3 pieces of four scaled values (each the rounding of what the
+// previous ones left), one word each.
+__device__ __forceinline__ void split3(float a[4], uint32_t w[3]) {
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    w[p] = e4m3x4(a[0], a[1], a[2], a[3]);
+    if (p < 2) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[p]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[p]), true);
+      a[0] -= lo[0];
+      a[1] -= lo[1];
+      a[2] -= hi[0];
+      a[3] -= hi[1];
+    }
+  }
+}
+
+// Rotate one unit and write its A pieces in the mixed fp8 x fp4 operand order:
+// positions 16 L + s + 4 e (e = 0..3) form one 4-byte word (see the file
+// comment), four words per piece per lane. ss[t * Gp + g] = (2 / sc_g, T_g).
+// store = false computes without writing.
+__device__ __forceinline__ void rot_pieces(const RotIn &in, int Gp, int m, int g, int L, bool store, uint32_t *xa,
+                                           float2 *ss) {
+  RotUnit u = rot_unit(in, L);
   uint32_t *blk = xa + static_cast<size_t>(m * Gp + g) * (kSetBytes / 4);
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) {
     float a[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = v[s4 + 4 * e] * c;
+    for (int e = 0; e < 4; ++e) a[e] = u.v[s4 + 4 * e] * u.c;
     // word (kq_a, w) of the A layout that holds positions 16 L + s4 + 4 e
     const int r = sigma(s4), kqb = L >> 1;
     const int off = (2 * (kqb & 1) + (r >> 1)) * 8 + 4 * (kqb >> 1) + 2 * (r & 1) + (L & 1);
+    uint32_t w[3];
+    split3(a, w);
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const uint32_t word = e4m3x4(a[0], a[1], a[2], a[3]);
-      if (store) blk[piece_offset(p) / 4 + off] = word;
-      if (p < 2) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), true);
-        a[0] -= lo[0];
-        a[1] -= lo[1];
-        a[2] -= hi[0];
-        a[3] -= hi[1];
-      }
-    }
+    for (int p = 0; p < 3; ++p)
+      if (store) blk[piece_offset(p) / 4 + off] = w[p];
   }
-  if (store && L == 0) ss[m * Gp + g] = make_float2(__builtin_amdgcn_ldexpf(1.f, E - 7), first * 11.313708498984761f);
+  if (store && L == 0)
+    ss[m * Gp + g] = make_float2(__builtin_amdgcn_ldexpf(1.f, u.E - 7), u.first * 11.313708498984761f);
 }
 
 // Launch constants the host derives once (no integer division in the kernel).

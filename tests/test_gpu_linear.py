@@ -250,8 +250,10 @@ def test_large_scales_stay_finite(L, dev, bits, m):
 
 # ---------------------------------------------------------------- product-VQ
 
-@pytest.mark.parametrize("n,k", [(1, 128), (130, 512), (257, 1024), (257, 4096)])
-@pytest.mark.parametrize("m,path", [(1, 1), (3, 1), (16, 1), (1, 2), (40, 2), (64, 2), (129, 2)])
+# GEMV path: one to four tokens at K a multiple of 512 run on the matrix cores,
+# the rest on the VALU lookup GEMV
+@pytest.mark.parametrize("n,k", [(1, 128), (17, 512), (130, 512), (257, 1024), (257, 4096)])
+@pytest.mark.parametrize("m,path", [(1, 1), (2, 1), (3, 1), (4, 1), (16, 1), (1, 2), (40, 2), (64, 2), (129, 2)])
 def test_pvq_small_shapes(L, dev, n, k, m, path):
     say(f"pvq n={n} k={k} m={m} path={path}")
     w, s, cb, idx, sc, pl = make_pvq(n, k, 16, n + k)
@@ -259,6 +261,22 @@ def test_pvq_small_shapes(L, dev, n, k, m, path):
     y = L.linear_forward(pl, to_dev(x, dev), path=path).cpu().numpy().astype(np.float64)
     want = oracle_pvq_rows(w, s, cb, x)
     assert O.rel_l2(y, want) < TOL
+
+
+@pytest.mark.parametrize("m", [2, 4])
+def test_pvq_tokens_of_very_different_size(L, dev, m):
+    """Each token's groups carry their own power-of-two scale into the matrix
+    cores (one A row per token piece); tokens 10^6 apart in size would expose
+    a scale applied to the wrong rows."""
+    n, k = 96, 1024
+    w, s, cb, idx, sc, pl = make_pvq(n, k, 16, 77)
+    x = synth.activations(m, k, workload=16, item=90 + m).astype(np.float64)
+    x *= (10.0 ** np.array([3, -3, 1, -1][:m]))[:, None]
+    x = x.astype(np.float16)
+    y = L.linear_forward(pl, to_dev(x, dev)).cpu().numpy().astype(np.float64)
+    want = oracle_pvq_rows(w, s, cb, x)
+    for t in range(m):   # each token against its own size
+        assert O.rel_l2(y[t], want[t]) < TOL
 
 
 @pytest.mark.parametrize("m", synth.PVQ_LINEAR["M"])
