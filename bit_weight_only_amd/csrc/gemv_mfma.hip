@@ -51,6 +51,25 @@ using namespace mx;
 
 constexpr int kMxMaxThreads = 1024;
 
+// Scale/zero pairs staged in LDS as fp32 (s, s z), one row of the workgroup's
+// tiles per MS pairs. A lane reads the GB pairs of its row and batch at once;
+// the sixteen rows of a tile land in distinct bank groups when the row stride
+// is an odd number of the read's width (8 bytes at GB = 1, 16 bytes otherwise).
+template <int GB>
+__host__ __device__ constexpr int fp32_meta_stride(int G) {
+  return GB == 1 ? (G | 1) : ((G + 1) / 2 | 1) * 2;
+}
+// the largest over the code widths (LDS sizing before the width is known)
+inline int fp32_meta_stride_any(int G) {
+  const int a = fp32_meta_stride<1>(G), b = fp32_meta_stride<2>(G);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float4 meta_pair(uint32_t w0, uint32_t w1) {
+  const float s0 = f16_bits_to_f32(w0 & 0xFFFFu), z0 = f16_bits_to_f32(w0 >> 16);
+  const float s1 = f16_bits_to_f32(w1 & 0xFFFFu), z1 = f16_bits_to_f32(w1 >> 16);
+  return make_float4(s0, s0 * z0, s1, s1 * z1);
+}
+
 // x: raw activations [M][K] fp16 (M <= 4); signs: [K] int8 (+-1), 16-byte aligned.
 template <int BITS, int DEPTH>
 __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *__restrict__ planes,
@@ -72,12 +91,13 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
 
   // LDS: piece sets [M][Gp] (kSetBytes each; groups past G zero), (2/sc, T) per
   // (token, group) [M][Gp] (past G zero), the waves' row partial sums
-  // [nw][M][rows], the meta words of this workgroup's rows [rows][meta_stride(G)].
-  const int MS = meta_stride(G);
+  // [nw][M][rows], the scale and scale x zero of this workgroup's rows as fp32
+  // pairs [rows][MS] (MS = fp32_meta_stride(G, GB)).
+  const int MS = fp32_meta_stride<GB>(G);
   uint32_t *xa = smem;
   float2 *ss = reinterpret_cast<float2 *>(xa + M * Gp * (kSetBytes / 4));
   float *yl = reinterpret_cast<float *>(ss + M * Gp);
-  uint32_t *ml = reinterpret_cast<uint32_t *>(yl + nw * M * rows);
+  float2 *ml = reinterpret_cast<float2 *>(yl + nw * M * rows);
 
   // All first-round loads go out before anything waits: the activations of the
   // first rotation pass, the code items (ring slots), the first pass of the
@@ -112,15 +132,6 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
   const int units = M * G, ustep = static_cast<int>(blockDim.x >> 3);
   const int u0 = rot_unit_of(static_cast<int>(threadIdx.x)), rL = rot_lane_of(static_cast<int>(threadIdx.x));
   const int m0 = (u0 >= G) + (u0 >= 2 * G) + (u0 >= 3 * G);
-  const RotIn rin = rot_load(xrs, srs, K, m0, u0 - m0 * G, rL, u0 < units);
-  __builtin_amdgcn_sched_barrier(0);   // the activations go out first: the rotation waits on them only
-  MxItem<BITS> ring[DEPTH];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    load(ring[d]);
-    __builtin_amdgcn_sched_barrier(0);   // keep the slots' loads in slot order, as in the loop
-  }
-
   // meta staging in 16-byte vectors (G % 4 == 0): tile k (rows 16 (b + k grid)
   // .. +15) is 16 G contiguous words of the meta array
   const int per_tile = 4 * G, n_meta = ntl * per_tile;
@@ -133,16 +144,60 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
   auto meta_store = [&](int i, uint4 v4) {
     const int k = i / per_tile, v = i - k * per_tile;
     const int w = v * 4, r = w / G, c = w - r * G;   // row r of tile k, word c (a vector never spans rows)
-    *reinterpret_cast<uint4 *>(ml + (k * 16 + r) * MS + c) = v4;
+    float2 *dst = ml + (k * 16 + r) * MS + c;   // 8-byte aligned (MS may be odd)
+    const float4 p0 = meta_pair(v4.x, v4.y), p1 = meta_pair(v4.z, v4.w);
+    dst[0] = make_float2(p0.x, p0.y);
+    dst[1] = make_float2(p0.z, p0.w);
+    dst[2] = make_float2(p1.x, p1.y);
+    dst[3] = make_float2(p1.z, p1.w);
   };
-  const uint4 mv0 = meta_load(static_cast<int>(threadIdx.x));
-
-  // the first pass runs on every lane (its loads must not be sunk into a branch);
-  // lanes without a unit compute on zeros and store nothing
-  rot_pieces(rin, Gp, min(m0, M - 1), u0 - m0 * G, rL, u0 < units, xa, ss);
-  for (int u = u0 + ustep; u < units; u += ustep) {
-    const int m = (u >= G) + (u >= 2 * G) + (u >= 3 * G), g = u - m * G;
-    rot_pieces(rot_load(xrs, srs, K, m, g, rL, true), Gp, m, g, rL, true, xa, ss);
+  // Order of the first loads. Every wave's activations and first scale/zero
+  // words go out before any wave's code loads: a compute unit's vector memory
+  // path returns data in request order, so the prologue would otherwise wait
+  // for the code loads' trip to HBM (the barrier waits for no data). Waves that
+  // rotate then issue two ring slots, rotate, and issue the rest (issuing a load
+  // stalls the wave while the unit's address queue is full, and the rotation is
+  // the prologue's critical path); waves without rotation units issue every
+  // slot at once. Both branches leave the same loads outstanding in the same
+  // order, and each wave passes one barrier.
+  constexpr int kEarly = DEPTH < 2 ? DEPTH : 2;
+  const bool rotating = wv * 8 < units;   // wave-uniform: the wave's first unit exists
+  MxItem<BITS> ring[DEPTH];
+  uint4 mv0;
+  if (rotating) {
+    const RotIn rin = rot_load(xrs, srs, K, m0, u0 - m0 * G, rL, u0 < units);
+    mv0 = meta_load(static_cast<int>(threadIdx.x));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < kEarly; ++d) {
+      load(ring[d]);
+      __builtin_amdgcn_sched_barrier(0);   // keep the slots' loads in slot order, as in the loop
+    }
+    // the first pass runs on every lane of the wave; lanes without a unit
+    // compute on zeros and store nothing
+    rot_pieces(rin, Gp, min(m0, M - 1), u0 - m0 * G, rL, u0 < units, xa, ss);
+    for (int u = u0 + ustep; u < units; u += ustep) {
+      const int m = (u >= G) + (u >= 2 * G) + (u >= 3 * G), g = u - m * G;
+      rot_pieces(rot_load(xrs, srs, K, m, g, rL, true), Gp, m, g, rL, true, xa, ss);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = kEarly; d < DEPTH; ++d) {
+      load(ring[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    mv0 = meta_load(static_cast<int>(threadIdx.x));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      load(ring[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   if (static_cast<int>(threadIdx.x) < n_meta) meta_store(static_cast<int>(threadIdx.x), mv0);
   for (int i = static_cast<int>(threadIdx.x + blockDim.x); i < n_meta; i += static_cast<int>(blockDim.x))
@@ -178,6 +233,7 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
   const uint32_t s_base = static_cast<uint32_t>(reinterpret_cast<const char *>(ss) - lds) +
                           static_cast<uint32_t>(min(kq, M - 1) * Gp * 8);
   float *ylane = yl + (wv * M + kq) * rows + j;   // this wave's partial sums (one per tile it touches)
+  const float2 *mlane = ml + j * MS;
 
   float yacc = 0.f;
   auto process = [&](const MxItem<BITS> &it) {
@@ -192,7 +248,7 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
       transpose4(w[a][0], w[a][1], w[a][2], w[a][3]);
     }
     const uint32_t a0off = a_base + static_cast<uint32_t>(g0) * a_step;
-    const uint32_t *mrow = ml + (pc.tile * 16 + j) * MS + g0;   // meta words of this lane's row
+    const float2 *mrow = mlane + (pc.tile * 16 * MS + g0);   // this lane's row: (s, s z) of the batch's groups
     float2 st[GB];
 #pragma unroll
     for (int u = 0; u < GB; u += 2) {
@@ -235,9 +291,9 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
       // groups past G: zero pieces and zero (2/sc, T), so the term vanishes (their
       // codes are the next row's)
       const float d = acc[u][0] + acc[u][1] + acc[u][2];
-      const uint32_t mt = mrow[min(u, G - 1 - g0)];   // groups past G: any finite word (the term is zero)
-      const float sc = f16_bits_to_f32(mt & 0xFFFFu), z = f16_bits_to_f32(mt >> 16);
-      yacc = fmaf(sc, fmaf(d, st[u].x, -z * st[u].y), yacc);
+      const float2 sz = mrow[u];   // K a multiple of 512: no padding groups
+      yacc = fmaf(sz.x, d * st[u].x, yacc);
+      yacc = fmaf(-sz.y, st[u].y, yacc);
     }
     // row tile done (the next item starts another tile, or this was the wave's last): add into LDS
     const int tile = pc.tile;
@@ -270,7 +326,7 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
 
 size_t mfma_lds_bytes(int M, int G, int Gp, int rows, int nw) {
   return static_cast<size_t>(M) * Gp * (kSetBytes + 8) + static_cast<size_t>(nw) * M * rows * 4 +
-         static_cast<size_t>(rows) * meta_stride(G) * 4;
+         static_cast<size_t>(rows) * fp32_meta_stride_any(G) * 8;
 }
 
 template <int BITS, int DEPTH>
@@ -315,11 +371,16 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 void gemv_mfma_shape(int M, int K, int N, int bits, int &grid, int &block, int &depth) {
   const int G = K / kGroup, T = (N + 15) / 16;
-  // eight waves rotate up to 64 (token, group) units in one pass; more units take sixteen
-  block = M * G <= 64 ? 512 : kMxMaxThreads;
-  // two workgroups per compute unit when there are many tiles and the workgroups are small
-  grid = (block == 512 && T >= 4 * kComputeUnits) ? 2 * kComputeUnits : (T < kComputeUnits ? T : kComputeUnits);
-  depth = bits == 4 ? 3 : 2;
+  // One workgroup per compute unit. Eight waves rotate up to 64 (token, group)
+  // units in one pass and suit up to one tile per workgroup; larger rotations
+  // or more tiles take sixteen (measured on the dense-stack shapes).
+  block = (M * G <= 64 && T <= kComputeUnits) ? 512 : kMxMaxThreads;
+  grid = T < kComputeUnits ? T : kComputeUnits;
+  // very tall matrices: more workgroups until a workgroup's rows fit in LDS
+  while (grid < T && mfma_lds_bytes(M, G, padded_groups(G, 3), ((T + grid - 1) / grid) * 16, block / 64) > kMaxLds)
+    grid = grid * 2 < T ? grid * 2 : T;
+  // ring depth: a third slot pays once each wave streams several tiles
+  depth = bits == 3 ? 2 : (bits == 4 || T >= 4 * kComputeUnits) ? 3 : 2;
 }
 
 bool gemv_mfma_supported(int M, int K, int N) {

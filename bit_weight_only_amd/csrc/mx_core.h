@@ -116,6 +116,34 @@ constexpr int kDppXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]
 constexpr int kDppXor8 = 0x128;   // row_ror 8: lane ^ 8 inside a 16-lane row
 
+// One cross-lane butterfly stage over sixteen values: v += sg * (v of the
+// partner lane), each a single v_fmac_f32 with a DPP source (partner lane ^ 1,
+// ^ 2 or ^ 8 for STAGE 0, 1, 2). Written out because the compiler keeps the DPP
+// move and the multiply-add apart (two instructions and a hazard wait each).
+// The leading s_nop covers the DPP read-after-VALU-write hazard of values the
+// compiler wrote just before; inside the block each value is read sixteen
+// instructions after its last write.
+#define LBQ_FMAC_DPP(I, CTRL) "v_fmac_f32_dpp %" #I ", %" #I ", %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"
+#define LBQ_FMAC_DPP16(CTRL)                                                                                        \
+  "s_nop 1\n\t" LBQ_FMAC_DPP(0, CTRL) LBQ_FMAC_DPP(1, CTRL) LBQ_FMAC_DPP(2, CTRL) LBQ_FMAC_DPP(3, CTRL)            \
+      LBQ_FMAC_DPP(4, CTRL) LBQ_FMAC_DPP(5, CTRL) LBQ_FMAC_DPP(6, CTRL) LBQ_FMAC_DPP(7, CTRL) LBQ_FMAC_DPP(8, CTRL)   \
+          LBQ_FMAC_DPP(9, CTRL) LBQ_FMAC_DPP(10, CTRL) LBQ_FMAC_DPP(11, CTRL) LBQ_FMAC_DPP(12, CTRL)                  \
+              LBQ_FMAC_DPP(13, CTRL) LBQ_FMAC_DPP(14, CTRL) LBQ_FMAC_DPP(15, CTRL)
+template <int STAGE>
+__device__ __forceinline__ void dpp_butterfly16(float v[16], float sg) {
+  static_assert(STAGE >= 0 && STAGE < 3, "stage");
+#define LBQ_DPP_OPERANDS                                                                                             \
+  : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]),      \
+    "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])                       \
+  : "v"(sg)
+  if constexpr (STAGE == 0) asm volatile(LBQ_FMAC_DPP16("quad_perm:[1,0,3,2]") LBQ_DPP_OPERANDS);
+  else if constexpr (STAGE == 1) asm volatile(LBQ_FMAC_DPP16("quad_perm:[2,3,0,1]") LBQ_DPP_OPERANDS);
+  else asm volatile(LBQ_FMAC_DPP16("row_ror:8") LBQ_DPP_OPERANDS);
+#undef LBQ_DPP_OPERANDS
+}
+#undef LBQ_FMAC_DPP16
+#undef LBQ_FMAC_DPP
+
 // Buffer loads (an offset past the end returns zeros): lanes without a unit
 // pass ok = false and load nothing.
 struct RotIn {
@@ -165,21 +193,9 @@ __device__ __forceinline__ RotUnit rot_unit(const RotIn &in, int L) {
     v[2 * i + 1] = half_hi(h);
   }
   u.first = v[0];   // s_0 x_0 on lane 0
-  {
-    const float sg = (L & 1) ? -1.f : 1.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = fmaf(dpp_f<kDppXor1>(v[i]), sg, v[i]);
-  }
-  {
-    const float sg = (L & 2) ? -1.f : 1.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = fmaf(dpp_f<kDppXor2>(v[i]), sg, v[i]);
-  }
-  {
-    const float sg = (L & 4) ? -1.f : 1.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = fmaf(dpp_f<kDppXor8>(v[i]), sg, v[i]);
-  }
+  dpp_butterfly16<0>(v, (L & 1) ? -1.f : 1.f);
+  dpp_butterfly16<1>(v, (L & 2) ? -1.f : 1.f);
+  dpp_butterfly16<2>(v, (L & 4) ? -1.f : 1.f);
 #pragma unroll
   for (int hw = 1; hw < 16; hw <<= 1) {
 #pragma unroll
