@@ -187,8 +187,11 @@ __device__ __forceinline__ RotUnit rot_unit(const RotIn &in, int L) {
   const uint32_t sw[4] = {in.sv.x, in.sv.y, in.sv.z, in.sv.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t sb = sw[i >> 1] >> (16 * (i & 1));   // sign bytes of elements 2i, 2i + 1
-    const uint32_t h = xw[i] ^ (((sb & 0x80u) << 8) | ((sb & 0x8000u) << 16));
+    // sign bytes of elements 2i, 2i + 1 moved to bytes 1 and 3 (their bit 7 onto
+    // the fp16 sign bits 15 and 31); selector 0x0C gives a zero byte
+    const uint32_t sel = (i & 1) ? 0x030C020Cu : 0x010C000Cu;
+    const uint32_t sb = __builtin_amdgcn_perm(sw[i >> 1], sw[i >> 1], sel);
+    const uint32_t h = xw[i] ^ (sb & 0x80008000u);
     v[2 * i] = half_lo(h);
     v[2 * i + 1] = half_hi(h);
   }
@@ -210,9 +213,13 @@ __device__ __forceinline__ RotUnit rot_unit(const RotIn &in, int L) {
   float mx = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[i]));
-  mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
-  mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
-  mx = fmaxf(mx, dpp_f<kDppXor8>(mx));
+  // across the unit's lanes on the bit patterns (non-negative floats order as
+  // unsigned integers; no NaN quieting needed)
+  uint32_t mb = __builtin_bit_cast(uint32_t, mx);
+  mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(mb), kDppXor1, 0xF, 0xF, true)));
+  mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(mb), kDppXor2, 0xF, 0xF, true)));
+  mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(mb), kDppXor8, 0xF, 0xF, true)));
+  mx = __builtin_bit_cast(float, mb);
   u.E = __builtin_amdgcn_frexp_expf(mx * kInvSqrt128);
   const float flip = (__builtin_popcount(L) & 1) ? -1.f : 1.f;
   u.c = __builtin_amdgcn_ldexpf(flip * kInvSqrt128, 8 - u.E);
