@@ -26,7 +26,7 @@ namespace {
 
 using namespace mx;
 
-constexpr int kPvqThreads = 512;
+constexpr int kPvqMaxThreads = 1024;
 constexpr int kGB = 2;   // groups per item: 64 index bytes of a row, 16 bytes per lane
 
 // Rotate one unit and write its A pieces in the product-VQ element order:
@@ -53,7 +53,7 @@ __device__ __forceinline__ void rot_pieces_pvq(const RotIn &in, int Gp, int m, i
 
 // x: raw activations [M][K] fp16 (M <= 4); signs: [K] int8 (+-1), 16-byte aligned.
 template <int DEPTH>
-__global__ void __launch_bounds__(kPvqThreads) gemv_pvq_mx_kernel(const uint4 *__restrict__ idx,
+__global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4 *__restrict__ idx,
                                                                   const uint16_t *__restrict__ row_scale,
                                                                   const uint32_t *__restrict__ codebook,
                                                                   const uint4 *__restrict__ x,
@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(kPvqThreads) gemv_pvq_mx_kernel(const uint4 *_
   const int ntl = sh.tq + (b < sh.tr ? 1 : 0);   // this workgroup's tiles: b + k grid, k < ntl
   const int rows = ntl * 16;
   const int items = ntl * sh.NB;
-  constexpr int nw = kPvqThreads / 64;
+  const int nw = static_cast<int>(blockDim.x >> 6), nt = static_cast<int>(blockDim.x);
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));   // wave-uniform
   const int lane = static_cast<int>(threadIdx.x & 63), j = lane & 15, kq = lane >> 4;
 
@@ -98,32 +98,62 @@ __global__ void __launch_bounds__(kPvqThreads) gemv_pvq_mx_kernel(const uint4 *_
     it = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, pbase + pstep, 0, 0));
     lc.advance(sh, nw);
   };
-  const int units = M * G, ustep = kPvqThreads >> 3;
+  const int units = M * G, ustep = nt >> 3;
   const int u0 = rot_unit_of(static_cast<int>(threadIdx.x)), rL = rot_lane_of(static_cast<int>(threadIdx.x));
   const int m0 = (u0 >= G) + (u0 >= 2 * G) + (u0 >= 3 * G);
-  const RotIn rin = rot_load(xrs, srs, K, min(m0, M - 1), u0 - m0 * G, rL, u0 < units);
-  __builtin_amdgcn_sched_barrier(0);   // the activations go out first: the rotation waits on them only
+  // Order of the first loads (a compute unit's vector memory path returns data
+  // in request order): every wave's activations and the codebook word go out
+  // first, all waves pass one barrier that waits for no data, then the index
+  // loads. Waves that rotate issue two ring slots, rotate, and issue the rest;
+  // the others skip the rotation and issue every slot at once. Both branches
+  // leave the same loads outstanding in the same order.
+  constexpr int kEarly = DEPTH < 2 ? DEPTH : 2;
+  const bool rotating = wv * 8 < units;   // wave-uniform
   uint4 ring[DEPTH];
+  uint32_t cw;
+  if (rotating) {
+    const RotIn rin = rot_load(xrs, srs, K, min(m0, M - 1), u0 - m0 * G, rL, u0 < units);
+    cw = codebook[threadIdx.x & 255];
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    load(ring[d]);
-    __builtin_amdgcn_sched_barrier(0);   // keep the slots' loads in slot order, as in the loop
+    for (int d = 0; d < kEarly; ++d) {
+      load(ring[d]);
+      __builtin_amdgcn_sched_barrier(0);   // keep the slots' loads in slot order, as in the loop
+    }
+    // the first pass runs on every lane of the wave; lanes without a unit
+    // compute on zeros and store nothing
+    rot_pieces_pvq(rin, Gp, min(m0, M - 1), u0 - m0 * G, rL, u0 < units, xa, sx);
+    for (int u = u0 + ustep; u < units; u += ustep) {
+      const int m = (u >= G) + (u >= 2 * G) + (u >= 3 * G), g = u - m * G;
+      rot_pieces_pvq(rot_load(xrs, srs, K, m, g, rL, true), Gp, m, g, rL, true, xa, sx);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = kEarly; d < DEPTH; ++d) {
+      load(ring[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    cw = codebook[threadIdx.x & 255];
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      load(ring[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (threadIdx.x < 256) lut[threadIdx.x] = codebook[threadIdx.x];
-  // the first pass runs on every lane (its loads must not be sunk into a branch);
-  // lanes without a unit compute on zeros and store nothing
-  rot_pieces_pvq(rin, Gp, min(m0, M - 1), u0 - m0 * G, rL, u0 < units, xa, sx);
-  for (int u = u0 + ustep; u < units; u += ustep) {
-    const int m = (u >= G) + (u >= 2 * G) + (u >= 3 * G), g = u - m * G;
-    rot_pieces_pvq(rot_load(xrs, srs, K, m, g, rL, true), Gp, m, g, rL, true, xa, sx);
-  }
+  if (threadIdx.x < 256) lut[threadIdx.x] = cw;
   {   // every set's zero piece, the row sums
-    for (int i = static_cast<int>(threadIdx.x); i < M * G * (kPieceBytes / 16); i += kPvqThreads) {
+    for (int i = static_cast<int>(threadIdx.x); i < M * G * (kPieceBytes / 16); i += nt) {
       const int q = i / (kPieceBytes / 16);
       reinterpret_cast<uint4 *>(xa + q * (kSetBytes / 4) + piece_offset(3) / 4)[i - q * (kPieceBytes / 16)] =
           make_uint4(0, 0, 0, 0);
     }
-    for (int i = static_cast<int>(threadIdx.x); i < nw * M * rows; i += kPvqThreads) yl[i] = 0.f;
+    for (int i = static_cast<int>(threadIdx.x); i < nw * M * rows; i += nt) yl[i] = 0.f;
   }
   __syncthreads();
 
@@ -179,7 +209,7 @@ __global__ void __launch_bounds__(kPvqThreads) gemv_pvq_mx_kernel(const uint4 *_
   }
   __syncthreads();
   // the waves' partials summed in wave order, times the row scale
-  for (int i2 = static_cast<int>(threadIdx.x); i2 < M * rows; i2 += kPvqThreads) {
+  for (int i2 = static_cast<int>(threadIdx.x); i2 < M * rows; i2 += nt) {
     const int m = i2 / rows, r = i2 - m * rows, row = (b + (r >> 4) * sh.grid) * 16 + (r & 15);
     float s = 0.f;
     for (int w2 = 0; w2 < nw; ++w2) s += yl[w2 * M * rows + i2];
@@ -187,8 +217,8 @@ __global__ void __launch_bounds__(kPvqThreads) gemv_pvq_mx_kernel(const uint4 *_
   }
 }
 
-size_t pvq_mx_lds(int M, int G, int rows) {
-  return 1024 + static_cast<size_t>(M) * G * (kSetBytes + 4) + static_cast<size_t>(kPvqThreads / 64) * M * rows * 4;
+size_t pvq_mx_lds(int M, int G, int rows, int block) {
+  return 1024 + static_cast<size_t>(M) * G * (kSetBytes + 4) + static_cast<size_t>(block / 64) * M * rows * 4;
 }
 
 constexpr int kComputeUnits = 256;
@@ -198,6 +228,9 @@ int pvq_mx_grid(int N) {
   const int T = (N + 15) / 16;
   return T < kComputeUnits ? T : kComputeUnits;
 }
+// one workgroup per compute unit: eight waves for up to one tile each, sixteen
+// beyond (the matrix-core RTN GEMV's measured choice on the same tile counts)
+int pvq_mx_block(int N) { return (N + 15) / 16 <= kComputeUnits ? 512 : kPvqMaxThreads; }
 
 }  // namespace
 
@@ -206,7 +239,7 @@ bool gemv_pvq_mx_supported(int M, int K, int N) {
   if (M < 1 || M > 4 || K < 4 * kGroup || K % (4 * kGroup) != 0 || N < 1) return false;
   if (static_cast<long long>(N + 16) * (K / kGroup) * 32 >= static_cast<long long>(kOutOfRange)) return false;
   const int grid = pvq_mx_grid(N), T = (N + 15) / 16;
-  return pvq_mx_lds(M, K / kGroup, ((T + grid - 1) / grid) * 16) <= kMaxLds;
+  return pvq_mx_lds(M, K / kGroup, ((T + grid - 1) / grid) * 16, pvq_mx_block(N)) <= kMaxLds;
 }
 
 hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, const uint8_t *codebook,
@@ -216,15 +249,16 @@ hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, con
       (reinterpret_cast<uintptr_t>(codebook) & 3u) != 0 || !gemv_pvq_mx_supported(M, K, N))
     return hipErrorInvalidValue;
   const int grid = pvq_mx_grid(N);
-  const MxShape sh = make_shape(M, K, N, 2, grid, kPvqThreads);   // batches of two groups
-  const size_t lds = pvq_mx_lds(M, sh.G, (sh.tq + (sh.tr ? 1 : 0)) * 16);
+  const int block = pvq_mx_block(N);
+  const MxShape sh = make_shape(M, K, N, 2, grid, block);   // batches of two groups
+  const size_t lds = pvq_mx_lds(M, sh.G, (sh.tq + (sh.tr ? 1 : 0)) * 16, block);
   auto kern = gemv_pvq_mx_kernel<2>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kPvqThreads), lds, s, reinterpret_cast<const uint4 *>(idx), row_scale,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(block), lds, s, reinterpret_cast<const uint4 *>(idx), row_scale,
                      reinterpret_cast<const uint32_t *>(codebook), reinterpret_cast<const uint4 *>(x),
                      reinterpret_cast<const uint4 *>(signs), y, sh);
   return hipGetLastError();
