@@ -21,6 +21,7 @@
 #include "mx_core.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace lbq {
 
@@ -122,22 +123,29 @@ __device__ void expert_linear(const MoeMxArgs &a, int e, int b, uint32_t *smem) 
   };
 
   // meta staging of this workgroup's rows, once for all chunks (G % 4 == 0):
-  // tile k (rows 16 (b + k grid) .. +15) is 16 G contiguous words
-  {
-    const int per_tile = 4 * G, n_meta = ntl * per_tile;
-    for (int i = static_cast<int>(threadIdx.x); i < n_meta; i += kMoeMxThreads) {
-      const int k = i / per_tile, v = i - k * per_tile;
-      const uint32_t off = static_cast<uint32_t>(((b + k * sh.grid) * per_tile + v) * 16);
-      const uint4 v4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(mrs, off, 0, 0));
-      const int w = v * 4, r = w / G, c = w - r * G;   // row r of tile k, word c (a vector never spans rows)
-      *reinterpret_cast<uint4 *>(ml + (k * 16 + r) * MS + c) = v4;
-    }
-  }
+  // tile k (rows 16 (b + k grid) .. +15) is 16 G contiguous words. The first
+  // two vectors of each thread are loaded with the first chunk's activations
+  // and stored after its rotation; any further ones right there.
+  const int per_tile = 4 * G, n_meta = ntl * per_tile;
+  auto meta_load = [&](int i) {
+    const int k = i / per_tile, v = i - k * per_tile;
+    const uint32_t off = static_cast<uint32_t>(((b + k * sh.grid) * per_tile + v) * 16) +
+                         (i < n_meta ? 0u : kOutOfRange);
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(mrs, off, 0, 0));
+  };
+  auto meta_store = [&](int i, uint4 v4) {
+    const int k = i / per_tile, v = i - k * per_tile;
+    const int w = v * 4, r = w / G, c = w - r * G;   // row r of tile k, word c (a vector never spans rows)
+    *reinterpret_cast<uint4 *>(ml + (k * 16 + r) * MS + c) = v4;
+  };
+  const int t0 = static_cast<int>(threadIdx.x);
+  const uint4 mv0 = meta_load(t0), mv1 = meta_load(t0 + kMoeMxThreads);
 
   const int units_max = kChunk * G, ustep = kMoeMxThreads >> 3;
   const int u0 = rot_unit_of(static_cast<int>(threadIdx.x)), rL = rot_lane_of(static_cast<int>(threadIdx.x));
 
-  for (int c0 = 0; c0 < n_e; c0 += kChunk) {
+  auto chunk = [&](int c0, auto first_tag) {
+    constexpr bool kFirst = decltype(first_tag)::value;
     const int M = min(kChunk, n_e - c0);
     const int units = M * G;
     // gathered activation rows and output assignments of the chunk (uniform)
@@ -165,20 +173,52 @@ __device__ void expert_linear(const MoeMxArgs &a, int e, int b, uint32_t *smem) 
       lt += wrap;
     };
     const int m0 = (u0 >= G) + (u0 >= 2 * G) + (u0 >= 3 * G);
-    const RotIn rin = unit_load(row_of(min(m0, M - 1)), u0 - m0 * G, rL, u0 < units);
-    __builtin_amdgcn_sched_barrier(0);   // the activations go out first: the rotation waits on them only
+    // Order of the loads (a compute unit's vector memory path returns data in
+    // request order): every wave's activations go out first, all waves pass one
+    // barrier that waits for no data, then the code loads. Waves with rotation
+    // units issue two ring slots, rotate, and issue the rest; the others skip
+    // the rotation and issue every slot at once. Both branches leave the same
+    // loads outstanding in the same order.
+    constexpr int kEarly = DEPTH < 2 ? DEPTH : 2;
+    const bool rotating = wv * 8 < units;   // wave-uniform
     MxItem<BITS> ring[DEPTH];
+    if (rotating) {
+      const RotIn rin = unit_load(row_of(min(m0, M - 1)), u0 - m0 * G, rL, u0 < units);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      load(ring[d]);
-      __builtin_amdgcn_sched_barrier(0);   // keep the slots' loads in slot order, as in the loop
+      for (int d = 0; d < kEarly; ++d) {
+        load(ring[d]);
+        __builtin_amdgcn_sched_barrier(0);   // keep the slots' loads in slot order, as in the loop
+      }
+      // the first pass runs on every lane of the wave; lanes without a unit
+      // compute on zeros and store nothing
+      rot_pieces(rin, Gp, min(m0, M - 1), u0 - m0 * G, rL, u0 < units, xa, ss);
+      for (int u = u0 + ustep; u < units; u += ustep) {
+        const int m = (u >= G) + (u >= 2 * G) + (u >= 3 * G), g = u - m * G;
+        rot_pieces(unit_load(row_of(m), g, rL, true), Gp, m, g, rL, true, xa, ss);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = kEarly; d < DEPTH; ++d) {
+        load(ring[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        load(ring[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    // the first pass runs on every lane (its loads must not be sunk into a branch);
-    // lanes without a unit compute on zeros and store nothing
-    rot_pieces(rin, Gp, min(m0, M - 1), u0 - m0 * G, rL, u0 < units, xa, ss);
-    for (int u = u0 + ustep; u < units; u += ustep) {
-      const int m = (u >= G) + (u >= 2 * G) + (u >= 3 * G), g = u - m * G;
-      rot_pieces(unit_load(row_of(m), g, rL, true), Gp, m, g, rL, true, xa, ss);
+    if constexpr (kFirst) {
+      if (t0 < n_meta) meta_store(t0, mv0);
+      if (t0 + kMoeMxThreads < n_meta) meta_store(t0 + kMoeMxThreads, mv1);
+      for (int i = t0 + 2 * kMoeMxThreads; i < n_meta; i += kMoeMxThreads) meta_store(i, meta_load(i));
     }
     {   // zero the padding groups' pieces and sums, and every set's zero piece
       const int pad = (Gp - G) * kChunk;
@@ -293,7 +333,9 @@ __device__ void expert_linear(const MoeMxArgs &a, int e, int b, uint32_t *smem) 
       }
     }
     __syncthreads();   // the next chunk overwrites the pieces
-  }
+  };
+  chunk(0, std::true_type{});
+  for (int c0 = kChunk; c0 < n_e; c0 += kChunk) chunk(c0, std::false_type{});
 }
 
 template <bool SWIGLU>
