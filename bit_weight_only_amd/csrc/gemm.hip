@@ -292,26 +292,21 @@ void launch_pvq_nb(int mt, dim3 grid, const uint8_t *idx, const uint8_t *codeboo
 }  // namespace
 
 GemmPlan gemm_plan(int M, int K, int N) {
-  // Token tiles of 16, 32 or 64. Two row blocks per wave once that still gives
-  // >= 128 tiles, else one; with few tiles split K until about 192 workgroups
-  // run (384 for long rows at >= 64 tokens); with many tiles at >= 64 tokens
-  // split 2 (4 for long rows) unless there are >= 512 tiles. Every slice keeps
-  // at least four groups.
+  // Token tiles of 16, 32 or 64. Two row blocks per wave only with >= 512 such
+  // tiles, else one; then split K until about 768 workgroups run at up to 16
+  // tokens and 384 beyond, every slice keeping at least four groups (measured
+  // on the product-VQ 4096 -> 14336 shape at 16 and 64 tokens).
   GemmPlan p;
   p.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   const int G = K / kGroup;
   p.m_tiles = M > 0 ? (M + 16 * p.mt - 1) / (16 * p.mt) : 0;
   const long tiles2 = static_cast<long>((N + 127) / 128) * p.m_tiles;
-  p.nb = tiles2 >= 128 ? 2 : 1;
+  p.nb = tiles2 >= 512 ? 2 : 1;
   p.n_tiles = (N + 64 * p.nb - 1) / (64 * p.nb);
   const long tiles = static_cast<long>(p.n_tiles) * p.m_tiles;
+  const long target = M <= 16 ? 768 : 384;
   p.S = 1;
-  if (p.nb == 2) {
-    if (M >= 64 && tiles < 512) p.S = G > 64 ? 4 : 2;
-  } else {
-    const long target = (M >= 64 && G > 64) ? 384 : 192;
-    while (tiles * p.S < target && p.S < 16) p.S *= 2;
-  }
+  while (tiles * p.S < target && p.S < 16) p.S *= 2;
   while (p.S > 1 && p.S * 4 > G) p.S /= 2;
   return p;
 }
