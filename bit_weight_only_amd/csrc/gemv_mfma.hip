@@ -303,17 +303,28 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
       yacc = 0.f;
     }
   };
-  // ring slot d holds items d, d + DEPTH, ... of the wave's sequence. Every
-  // slot is refilled on every pass, also past the wave's last item, and only
-  // the processing is skipped there: the loads stay unconditional and in one
-  // fixed order, so the compiler keeps exact wait counts.
-  for (int i = wv; i < items; i += DEPTH * nw) {
+  // ring slot d holds items d, d + DEPTH, ... of the wave's sequence. Full
+  // passes refill every slot unconditionally, in one fixed order, so the
+  // compiler keeps exact wait counts; the last pass refills only slots with an
+  // item left and the drain processes them, so no load goes past the end (each
+  // costs address-unit time even when it returns zeros).
+  const int nwi = items > wv ? (items - wv + nw - 1) / nw : 0;   // this wave's items
+  int k = 0;
+  for (; k + 2 * DEPTH <= nwi; k += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-      if (d == 0 || i + d * nw < items) process(ring[d]);
+      process(ring[d]);
       load(ring[d]);
     }
   }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    if (k + d < nwi) process(ring[d]);
+    if (k + d + DEPTH < nwi) load(ring[d]);
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (k + DEPTH + d < nwi) process(ring[d]);
   __syncthreads();
   // the waves' partials summed in wave order: the result does not depend on timing
   for (int idx = static_cast<int>(threadIdx.x); idx < M * rows; idx += static_cast<int>(blockDim.x)) {
@@ -379,8 +390,8 @@ void gemv_mfma_shape(int M, int K, int N, int bits, int &grid, int &block, int &
   // very tall matrices: more workgroups until a workgroup's rows fit in LDS
   while (grid < T && mfma_lds_bytes(M, G, padded_groups(G, 3), ((T + grid - 1) / grid) * 16, block / 64) > kMaxLds)
     grid = grid * 2 < T ? grid * 2 : T;
-  // ring depth: a third slot pays once each wave streams several tiles
-  depth = bits == 3 ? 2 : (bits == 4 || T >= 4 * kComputeUnits) ? 3 : 2;
+  // ring depth: a third slot pays once each wave streams several tiles or long rows
+  depth = bits == 3 ? 2 : (bits == 4 || T >= 4 * kComputeUnits || G >= 64) ? 3 : 2;
 }
 
 bool gemv_mfma_supported(int M, int K, int N) {
