@@ -71,15 +71,17 @@ __device__ __forceinline__ float4 meta_pair(uint32_t w0, uint32_t w1) {
 }
 
 // x: raw activations [M][K] fp16 (M <= 4); signs: [K] int8 (+-1), 16-byte aligned.
-template <int BITS, int DEPTH>
+// PASSES: the tokens go in passes of mp (else all M in one, mp == M).
+template <int BITS, int DEPTH, bool PASSES>
 __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *__restrict__ planes,
                                                                  const uint32_t *__restrict__ meta,
                                                                  const uint4 *__restrict__ x,
                                                                  const uint4 *__restrict__ signs,
-                                                                 uint16_t *__restrict__ y, const MxShape sh) {
+                                                                 uint16_t *__restrict__ y, const MxShape sh,
+                                                                 const int mp) {
   constexpr int GB = MxBatch<BITS>::GB, NV = MxBatch<BITS>::NV;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-  const int M = sh.M, K = sh.K, N = sh.N, G = sh.G, Gp = sh.Gp;
+  const int K = sh.K, N = sh.N, G = sh.G, Gp = sh.Gp;
   const int VR = G * BITS;                       // 16-byte plane vectors per row
   const int b = static_cast<int>(blockIdx.x);
   const int ntl = sh.tq + (b < sh.tr ? 1 : 0);   // this workgroup's tiles: b + k grid, k < ntl
@@ -89,15 +91,23 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));   // wave-uniform
   const int lane = static_cast<int>(threadIdx.x & 63), j = lane & 15, kq = lane >> 4;
 
-  // LDS: piece sets [M][Gp] (kSetBytes each; groups past G zero), (2/sc, T) per
-  // (token, group) [M][Gp] (past G zero), the waves' row partial sums
-  // [nw][M][rows], the scale and scale x zero of this workgroup's rows as fp32
-  // pairs [rows][MS] (MS = fp32_meta_stride(G, GB)).
+  // The tokens go in passes of up to mp (all of them when their pieces fit in
+  // LDS; a later pass re-reads the codes, mostly from L2). LDS, sized for mp
+  // tokens: piece sets [mp][Gp] (kSetBytes each; groups past G zero), (2/sc, T)
+  // per (token, group) [mp][Gp] (past G zero), the waves' row partial sums
+  // [nw][mp][rows], and, staged once by the first pass, the scale and scale x
+  // zero of this workgroup's rows as fp32 pairs [rows][MS] (MS =
+  // fp32_meta_stride(G, GB)).
   const int MS = fp32_meta_stride<GB>(G);
   uint32_t *xa = smem;
-  float2 *ss = reinterpret_cast<float2 *>(xa + M * Gp * (kSetBytes / 4));
-  float *yl = reinterpret_cast<float *>(ss + M * Gp);
-  float2 *ml = reinterpret_cast<float2 *>(yl + nw * M * rows);
+  float2 *ss = reinterpret_cast<float2 *>(xa + mp * Gp * (kSetBytes / 4));
+  float *yl = reinterpret_cast<float *>(ss + mp * Gp);
+  float2 *ml = reinterpret_cast<float2 *>(yl + nw * mp * rows);
+  const int npass = PASSES ? (sh.M + mp - 1) / mp : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+  const int t0 = PASSES ? pass * mp : 0;
+  const int M = PASSES ? min(mp, sh.M - t0) : sh.M;
+  const bool first = pass == 0;
 
   // All first-round loads go out before anything waits: the activations of the
   // first rotation pass, the code items (ring slots), the first pass of the
@@ -109,7 +119,7 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
   const __amdgpu_buffer_rsrc_t mrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(meta), 0, N * G * 4, kBufferFlags);
   const __amdgpu_buffer_rsrc_t xrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4 *>(x), 0, M * K * 2, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4 *>(x + t0 * (K / 8)), 0, M * K * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t srs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4 *>(signs), 0, K, kBufferFlags);
   const uint32_t pbase = static_cast<uint32_t>(((b * 16 + j) * VR + kq) * 16);
@@ -134,7 +144,7 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
   const int m0 = (u0 >= G) + (u0 >= 2 * G) + (u0 >= 3 * G);
   // meta staging in 16-byte vectors (G % 4 == 0): tile k (rows 16 (b + k grid)
   // .. +15) is 16 G contiguous words of the meta array
-  const int per_tile = 4 * G, n_meta = ntl * per_tile;
+  const int per_tile = 4 * G, n_meta = first ? ntl * per_tile : 0;   // the first pass stages them
   auto meta_load = [&](int i) {
     const int k = i / per_tile, v = i - k * per_tile;
     const uint32_t off = static_cast<uint32_t>(((b + k * sh.grid) * per_tile + v) * 16) +
@@ -331,7 +341,9 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
     const int m = idx / rows, r = idx - m * rows, row = (b + (r >> 4) * sh.grid) * 16 + (r & 15);
     float acc = 0.f;
     for (int w = 0; w < nw; ++w) acc += yl[w * M * rows + idx];
-    if (row < N) y[static_cast<size_t>(m) * N + row] = f32_to_f16_bits(acc);
+    if (row < N) y[static_cast<size_t>(t0 + m) * N + row] = f32_to_f16_bits(acc);
+  }
+  if (PASSES) __syncthreads();   // the next pass overwrites the pieces and partial sums
   }
 }
 
@@ -342,10 +354,11 @@ size_t mfma_lds_bytes(int M, int G, int Gp, int rows, int nw) {
 
 template <int BITS, int DEPTH>
 hipError_t launch_depth(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs, uint16_t *y,
-                        const MxShape &sh, int grid, int block, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+                        const MxShape &sh, int grid, int block, int mp, hipStream_t s, hipEvent_t start,
+                        hipEvent_t stop) {
   const int rows = (sh.tq + (sh.tr ? 1 : 0)) * 16;
-  const size_t lds = mfma_lds_bytes(sh.M, sh.G, sh.Gp, rows, block / 64);
-  auto kern = gemv_mfma_kernel<BITS, DEPTH>;
+  const size_t lds = mfma_lds_bytes(mp, sh.G, sh.Gp, rows, block / 64);
+  auto kern = mp < sh.M ? gemv_mfma_kernel<BITS, DEPTH, true> : gemv_mfma_kernel<BITS, DEPTH, false>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -357,26 +370,38 @@ hipError_t launch_depth(const void *planes, const void *meta, const uint16_t *x,
   const uint4 *sv = reinterpret_cast<const uint4 *>(signs);
   if (start || stop)   // the events take this kernel's own begin / end times
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(block), static_cast<uint32_t>(lds), s, start, stop, 0, pl, mt, xv,
-                          sv, y, sh);
+                          sv, y, sh, mp);
   else
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(block), lds, s, pl, mt, xv, sv, y, sh);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(block), lds, s, pl, mt, xv, sv, y, sh, mp);
   return hipGetLastError();
 }
 
 template <int BITS>
 hipError_t launch_bits(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs, uint16_t *y,
-                       const MxShape &sh, int grid, int block, int depth, hipStream_t s, hipEvent_t start,
+                       const MxShape &sh, int grid, int block, int depth, int mp, hipStream_t s, hipEvent_t start,
                        hipEvent_t stop) {
   switch (depth) {
-    case 1: return launch_depth<BITS, 1>(planes, meta, x, signs, y, sh, grid, block, s, start, stop);
-    case 2: return launch_depth<BITS, 2>(planes, meta, x, signs, y, sh, grid, block, s, start, stop);
-    case 3: return launch_depth<BITS, 3>(planes, meta, x, signs, y, sh, grid, block, s, start, stop);
-    default: return launch_depth<BITS, 4>(planes, meta, x, signs, y, sh, grid, block, s, start, stop);
+    case 1: return launch_depth<BITS, 1>(planes, meta, x, signs, y, sh, grid, block, mp, s, start, stop);
+    case 2: return launch_depth<BITS, 2>(planes, meta, x, signs, y, sh, grid, block, mp, s, start, stop);
+    case 3: return launch_depth<BITS, 3>(planes, meta, x, signs, y, sh, grid, block, mp, s, start, stop);
+    default: return launch_depth<BITS, 4>(planes, meta, x, signs, y, sh, grid, block, mp, s, start, stop);
   }
 }
 
 constexpr int kComputeUnits = 256;
 constexpr size_t kMaxLds = 160 * 1024;
+
+}  // namespace
+
+namespace {
+
+// Tokens per pass: all of them when their pieces fit in LDS next to the
+// workgroup's rows, else two (a second pass re-reads the codes, mostly from L2);
+// 0 when not even that fits.
+int tokens_per_pass(int M, int G, int Gp, int rows, int nw) {
+  if (mfma_lds_bytes(M, G, Gp, rows, nw) <= kMaxLds) return M;
+  return (M > 2 && mfma_lds_bytes(2, G, Gp, rows, nw) <= kMaxLds) ? 2 : 0;
+}
 
 }  // namespace
 
@@ -388,7 +413,7 @@ void gemv_mfma_shape(int M, int K, int N, int bits, int &grid, int &block, int &
   block = (M * G <= 64 && T <= kComputeUnits) ? 512 : kMxMaxThreads;
   grid = T < kComputeUnits ? T : kComputeUnits;
   // very tall matrices: more workgroups until a workgroup's rows fit in LDS
-  while (grid < T && mfma_lds_bytes(M, G, padded_groups(G, 3), ((T + grid - 1) / grid) * 16, block / 64) > kMaxLds)
+  while (grid < T && tokens_per_pass(M, G, padded_groups(G, 3), ((T + grid - 1) / grid) * 16, block / 64) == 0)
     grid = grid * 2 < T ? grid * 2 : T;
   // ring depth: a third slot pays once each wave streams several tiles or long rows
   depth = bits == 3 ? 2 : (bits == 4 || T >= 4 * kComputeUnits || G >= 64) ? 3 : 2;
@@ -402,8 +427,7 @@ bool gemv_mfma_supported(int M, int K, int N) {
   int grid, block, depth;
   gemv_mfma_shape(M, K, N, 2, grid, block, depth);
   const int T = (N + 15) / 16;
-  return mfma_lds_bytes(M, K / kGroup, padded_groups(K / kGroup, 3), ((T + grid - 1) / grid) * 16, block / 64) <=
-         kMaxLds;
+  return tokens_per_pass(M, K / kGroup, padded_groups(K / kGroup, 3), ((T + grid - 1) / grid) * 16, block / 64) > 0;
 }
 
 hipError_t launch_gemv_mfma(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs,
@@ -419,11 +443,12 @@ hipError_t launch_gemv_mfma(const void *planes, const void *meta, const uint16_t
   if (depth <= 0) depth = d0;
   if (block % 64 != 0 || block < 64 || block > kMxMaxThreads || grid < 1) return hipErrorInvalidValue;
   const MxShape sh = make_shape(M, K, N, bits, grid, block);
-  if (mfma_lds_bytes(M, sh.G, sh.Gp, (sh.tq + (sh.tr ? 1 : 0)) * 16, block / 64) > kMaxLds) return hipErrorInvalidValue;
+  const int mp = tokens_per_pass(M, sh.G, sh.Gp, (sh.tq + (sh.tr ? 1 : 0)) * 16, block / 64);
+  if (mp == 0) return hipErrorInvalidValue;
   switch (bits) {
-    case 2: return launch_bits<2>(planes, meta, x, signs, y, sh, grid, block, depth, s, start, stop);
-    case 3: return launch_bits<3>(planes, meta, x, signs, y, sh, grid, block, depth, s, start, stop);
-    default: return launch_bits<4>(planes, meta, x, signs, y, sh, grid, block, depth, s, start, stop);
+    case 2: return launch_bits<2>(planes, meta, x, signs, y, sh, grid, block, depth, mp, s, start, stop);
+    case 3: return launch_bits<3>(planes, meta, x, signs, y, sh, grid, block, depth, mp, s, start, stop);
+    default: return launch_bits<4>(planes, meta, x, signs, y, sh, grid, block, depth, mp, s, start, stop);
   }
 }
 
