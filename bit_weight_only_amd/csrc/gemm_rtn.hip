@@ -22,9 +22,9 @@
 // when the tile grid alone leaves the chip idle). Per group:
 //  * the token tile's rotated activations (folded slot order: u32 slot c of a
 //    32-chunk = (x[c], x[c + 16])) are copied global -> LDS asynchronously into
-//    a ring of kRing slots, kRing - 1 groups ahead, one barrier per group;
+//    a ring of three slots, two groups ahead, one barrier per group;
 //  * each wave's code vectors and (s, z) words go straight into registers by
-//    buffer loads, kRing - 1 groups ahead (offsets past the end return zeros
+//    buffer loads, two groups ahead (offsets past the end return zeros
 //    without a memory access: rows past N, groups past the slice); a 4x4 lane
 //    transpose gives lane (j, kq) word column kq of every plane of its rows;
 //  * for k-step t, lane (i, kq) supplies slots 4t..4t+3 of token i's chunk kq
@@ -44,7 +44,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRing = 3;                        // activation slots; loads run kRing - 1 groups ahead
+// Ring slots: loads run kRing - 1 groups ahead. Deeper rings measured no
+// faster: at few tokens the loop is bound by the compute unit's vector-memory
+// address path (about one 128-byte line per few cycles), not by latency.
+constexpr int kRing = 3;
 constexpr int kBufferFlags = 0x00020000;        // buffer descriptor word 3 (32-bit data, no swizzle)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every supported size
 
@@ -204,6 +207,15 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
   };
 
   auto contract = [&](int q) {
+    // the group's A fragments first: their LDS latency overlaps the decode
+    const uint4 *slot = xs[q];
+    half8_t av[4][MT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        av[t][mt] = __builtin_bit_cast(half8_t, slot[(mt * 16 + j) * 16 + ((4 * kq + t) ^ j)]);
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t w[4 * T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -227,15 +239,8 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
       }
       decode_biased<BITS>(&w[nb * BITS], h[nb]);
     }
-    const uint4 *slot = xs[q];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      half8_t av[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int tok = mt * 16 + j;
-        av[mt] = __builtin_bit_cast(half8_t, slot[tok * 16 + ((4 * kq + t) ^ j)]);
-      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         uint32_t b[4];
@@ -245,7 +250,7 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
         const half8_t bop = __builtin_bit_cast(half8_t, make_uint4(b[0], b[1], b[2], b[3]));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], bop, acc[nb][mt], 0, 0, 0);
+          acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t][mt], bop, acc[nb][mt], 0, 0, 0);
       }
     }
   };
