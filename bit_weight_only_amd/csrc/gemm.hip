@@ -330,6 +330,8 @@ GemmPlan gemm_rtn_plan(int M, int K, int N) {
   const long target = 128L << ((G >= 64 ? 1 : 0) + (M >= 128 ? 1 : 0));
   p.S = 1;
   while (tiles * p.S < target && G / (2 * p.S) >= 8) p.S *= 2;
+  // slices short enough for the kernel to stage their scale/zero words in LDS
+  while ((G + p.S - 1) / p.S > gemm_rtn_meta_max_groups(p.nb)) p.S *= 2;
   return p;
 }
 

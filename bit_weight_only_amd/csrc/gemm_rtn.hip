@@ -23,10 +23,13 @@
 //  * the token tile's rotated activations (folded slot order: u32 slot c of a
 //    32-chunk = (x[c], x[c + 16])) are copied global -> LDS asynchronously into
 //    a ring of three slots, two groups ahead, one barrier per group;
-//  * each wave's code vectors and (s, z) words go straight into registers by
-//    buffer loads, two groups ahead (offsets past the end return zeros
-//    without a memory access: rows past N, groups past the slice); a 4x4 lane
-//    transpose gives lane (j, kq) word column kq of every plane of its rows;
+//  * each wave's code vectors go straight into registers by buffer loads, two
+//    groups ahead (offsets past the end return zeros without a memory access:
+//    rows past N, groups past the slice); a 4x4 lane transpose gives lane
+//    (j, kq) word column kq of every plane of its rows;
+//  * the (s, z) words of the workgroup's rows over its slice are staged in LDS
+//    once, in whole 16-byte vectors, before the loop (per group and row they
+//    would cost one 128-byte line request each for 4 bytes);
 //  * for k-step t, lane (i, kq) supplies slots 4t..4t+3 of token i's chunk kq
 //    as A and slots 4t..4t+3 of row j's word column kq as B, so both operands
 //    agree on which k each element is.
@@ -51,6 +54,16 @@ constexpr int kRing = 3;
 constexpr int kBufferFlags = 0x00020000;        // buffer descriptor word 3 (32-bit data, no swizzle)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every supported size
 
+// Slice length (groups) up to which the scale/zero words of a workgroup's rows
+// are staged in LDS (about 24 KB); the plans split K further when needed.
+__host__ __device__ constexpr int meta_max_groups(int nb) {
+  return nb == 1 ? 88 : nb == 2 ? 40 : 16;
+}
+// 16-byte meta vectors per row of a slice of ns groups (4-group aligned ends)
+__host__ __device__ constexpr int meta_vectors(int ns) {
+  return (ns + 6) / 4;
+}
+
 struct RtnGemmArgs {
   const uint4 *xf;         // rotated activations [M][K] fp16, folded slot order
   const uint4 *tz;         // [M][Gp / 4] of 4 u32: (T/16 high, T/16 low) fp16 per (token, group)
@@ -60,6 +73,7 @@ struct RtnGemmArgs {
   float *part;             // split-K partial tiles (S > 1)
   uint32_t *counters;      // split-K arrival counters, one per tile, zero on entry
   int M, K, N, S, Gp;
+  int MS;                  // LDS row stride (words) of the staged scale/zero words: 4 vectors + 1
 };
 
 __device__ __forceinline__ uint32_t pk_fma(uint32_t h, half2_t s2, half2_t c) {
@@ -132,12 +146,15 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
   constexpr int T = (U + 3) / 4;         // of them per lane
   constexpr int D = kRing - 1;           // groups in flight
   constexpr int CA = MT;                 // activation copies per wave per group (16 MT rows x 256 B)
-  constexpr int kLoads = CA + T + NB;    // vector-memory operations per wave per group
+  constexpr int kLoads = CA + T;         // vector-memory operations per wave per group
+  constexpr int kRowsWG = kWaves * 16 * NB;
+  constexpr int kMetaIters = (kRowsWG * meta_vectors(meta_max_groups(NB)) + kThreads - 1) / kThreads;
   constexpr int C = gemm_num_classes<BITS>();
   __shared__ __attribute__((aligned(16))) uint4 xs0[16 * MT * 16];
   __shared__ __attribute__((aligned(16))) uint4 xs1[16 * MT * 16];
   __shared__ __attribute__((aligned(16))) uint4 xs2[16 * MT * 16];
   uint4 *const xs[kRing] = {xs0, xs1, xs2};
+  extern __shared__ uint32_t msm[];   // [kRowsWG][a.MS]: (s, z) of group gb0 + c at column c
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -163,11 +180,18 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
     const int row = row0 + (u / BITS) * 16;
     poff[t] = (u < U && row < a.N) ? (static_cast<uint32_t>(row) * G * BITS + u % BITS) * 16 : kOutOfRange;
   }
-  uint32_t moff[NB];
+  // scale/zero staging loads: thread i + kThreads it takes vector v of local
+  // row r (consecutive threads, consecutive vectors of a row). Issued first, so
+  // they arrive ahead of the ring's loads.
+  const int gb0 = g0 & ~3;
+  const int nq = (((g1 + 3) & ~3) - gb0) / 4;
+  uint4 mst[kMetaIters];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int row = row0 + nb * 16;
-    moff[nb] = row < a.N ? static_cast<uint32_t>(row) * G * 4 : kOutOfRange;
+  for (int it = 0; it < kMetaIters; ++it) {
+    const int i = static_cast<int>(threadIdx.x) + it * kThreads;
+    const int r = i / nq, v = i - r * nq, row = blockIdx.y * kRowsWG + r;
+    const uint32_t off = (r < kRowsWG && row < a.N) ? (static_cast<uint32_t>(row) * G + gb0) * 4 + v * 16 : kOutOfRange;
+    mst[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(mrs, off, 0, 0));
   }
   // activation copies: wave w fills physical vectors [64 CA w, 64 CA (w + 1)) of
   // a slot. Logical column c of token t sits at physical column c ^ (t & 15), so
@@ -183,7 +207,6 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
   }
 
   uint4 bv[kRing][T];
-  uint32_t mv[kRing][NB];
   float4_t acc[NB][MT];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -201,12 +224,11 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
     for (int t = 0; t < T; ++t)
       bv[q][t] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, (poff[t] | past) + g * (BITS * 16), 0, 0));
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      mv[q][nb] = __builtin_amdgcn_raw_buffer_load_b32(mrs, (moff[nb] | past) + g * 4, 0, 0);
   };
+  // this lane's row of block nb in the staged scale/zero words
+  const uint32_t *mrow = msm + (wave * 16 * NB + j) * a.MS - gb0;
 
-  auto contract = [&](int q) {
+  auto contract = [&](int q, int g) {
     // the group's A fragments first: their LDS latency overlaps the decode
     const uint4 *slot = xs[q];
     half8_t av[4][MT];
@@ -230,7 +252,7 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
     uint32_t h[NB][16];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const _Float16 s = __builtin_bit_cast(half2_t, mv[q][nb])[0];
+      const _Float16 s = __builtin_bit_cast(half2_t, mrow[nb * 16 * a.MS + g])[0];
       s2[nb] = half2_t{s, s};
 #pragma unroll
       for (int c = 0; c < C; ++c) {
@@ -257,6 +279,19 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
 
 #pragma unroll
   for (int q = 0; q < D; ++q) issue(q, g0 + q);
+  // the staged words into LDS (visible after the loop's first barrier)
+#pragma unroll
+  for (int it = 0; it < kMetaIters; ++it) {
+    const int i = static_cast<int>(threadIdx.x) + it * kThreads;
+    const int r = i / nq, v = i - r * nq;
+    if (r < kRowsWG) {
+      uint32_t *dst = msm + r * a.MS + 4 * v;
+      dst[0] = mst[it].x;
+      dst[1] = mst[it].y;
+      dst[2] = mst[it].z;
+      dst[3] = mst[it].w;
+    }
+  }
   for (int g = g0; g < g1; g += kRing) {
 #pragma unroll
     for (int q = 0; q < kRing; ++q) {
@@ -266,7 +301,7 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
       wait_vm_lds<(D - 1) * kLoads>();
       __builtin_amdgcn_s_barrier();
       issue((q + D) % kRing, g + q + D);
-      if (g + q < g1) contract(q);
+      if (g + q < g1) contract(q, g + q);
     }
   }
 
@@ -285,8 +320,8 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int g = 16 * c16 + 4 * kq + e;
-        const half2_t sz = __builtin_bit_cast(half2_t, __builtin_amdgcn_raw_buffer_load_b32(mrs, moff[nb] + g * 4, 0, 0));
-        const _Float16 v = (g >= g0 && g < g1) ? static_cast<_Float16>(-16.0f) * (sz[0] * sz[1]) : static_cast<_Float16>(0.0f);
+        const half2_t sz = __builtin_bit_cast(half2_t, (g >= g0 && g < g1) ? mrow[nb * 16 * a.MS + g] : 0u);
+        const _Float16 v = static_cast<_Float16>(-16.0f) * (sz[0] * sz[1]);
         b[e] = __builtin_bit_cast(uint32_t, half2_t{v, v});
       }
       const half8_t bop = __builtin_bit_cast(half8_t, make_uint4(b[0], b[1], b[2], b[3]));
@@ -350,28 +385,41 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
 }
 
 template <int BITS, int NB, int MT>
-void launch_rtn(dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_rtn_kernel<BITS, NB, MT>), grid, dim3(kThreads), 0, s, a);
+hipError_t launch_rtn(dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(kWaves * 16 * NB) * a.MS * 4;
+  const size_t ring = static_cast<size_t>(kRing) * 16 * MT * 16 * 16;   // the static activation slots
+  auto kern = gemm_rtn_kernel<BITS, NB, MT>;
+  if (ring + lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
 }
 
 template <int BITS>
-void launch_rtn_bits(const GemmPlan &p, dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
+hipError_t launch_rtn_bits(const GemmPlan &p, dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
   if (p.nb == 4) {
-    if (p.mt == 1) launch_rtn<BITS, 4, 1>(grid, a, s);
-    else if (p.mt == 2) launch_rtn<BITS, 4, 2>(grid, a, s);
-    else launch_rtn<BITS, 4, 4>(grid, a, s);
-  } else if (p.nb == 2) {
-    if (p.mt == 1) launch_rtn<BITS, 2, 1>(grid, a, s);
-    else if (p.mt == 2) launch_rtn<BITS, 2, 2>(grid, a, s);
-    else launch_rtn<BITS, 2, 4>(grid, a, s);
-  } else {
-    if (p.mt == 1) launch_rtn<BITS, 1, 1>(grid, a, s);
-    else if (p.mt == 2) launch_rtn<BITS, 1, 2>(grid, a, s);
-    else launch_rtn<BITS, 1, 4>(grid, a, s);
+    if (p.mt == 1) return launch_rtn<BITS, 4, 1>(grid, a, s);
+    if (p.mt == 2) return launch_rtn<BITS, 4, 2>(grid, a, s);
+    return launch_rtn<BITS, 4, 4>(grid, a, s);
   }
+  if (p.nb == 2) {
+    if (p.mt == 1) return launch_rtn<BITS, 2, 1>(grid, a, s);
+    if (p.mt == 2) return launch_rtn<BITS, 2, 2>(grid, a, s);
+    return launch_rtn<BITS, 2, 4>(grid, a, s);
+  }
+  if (p.mt == 1) return launch_rtn<BITS, 1, 1>(grid, a, s);
+  if (p.mt == 2) return launch_rtn<BITS, 1, 2>(grid, a, s);
+  return launch_rtn<BITS, 1, 4>(grid, a, s);
 }
 
 }  // namespace
+
+int gemm_rtn_meta_max_groups(int nb) {
+  return meta_max_groups(nb);
+}
 
 int gemm_tz_stride(int K) {
   return (K / kGroup + 15) / 16 * 16;
@@ -388,6 +436,8 @@ hipError_t launch_gemm_rtn(const GemmPlan &p, int bits, const void *planes, cons
   if ((p.nb != 1 && p.nb != 2 && p.nb != 4) || (p.mt != 1 && p.mt != 2 && p.mt != 4) || p.S < 1)
     return hipErrorInvalidValue;
   if (bits < 2 || bits > 4 || !gemm_rtn_supported(K, N, bits)) return hipErrorInvalidValue;
+  const int G = K / kGroup, ns = (G + p.S - 1) / p.S;   // longest slice
+  if (p.S > G || ns > meta_max_groups(p.nb)) return hipErrorInvalidValue;
   RtnGemmArgs a;
   a.xf = reinterpret_cast<const uint4 *>(xf);
   a.tz = reinterpret_cast<const uint4 *>(tz);
@@ -401,13 +451,13 @@ hipError_t launch_gemm_rtn(const GemmPlan &p, int bits, const void *planes, cons
   a.N = N;
   a.S = p.S;
   a.Gp = gemm_tz_stride(K);
+  a.MS = 4 * meta_vectors(ns) + 1;
   const dim3 grid(static_cast<unsigned>(p.S), static_cast<unsigned>(p.n_tiles), static_cast<unsigned>(p.m_tiles));
   switch (bits) {
-    case 2: launch_rtn_bits<2>(p, grid, a, s); break;
-    case 3: launch_rtn_bits<3>(p, grid, a, s); break;
-    default: launch_rtn_bits<4>(p, grid, a, s); break;
+    case 2: return launch_rtn_bits<2>(p, grid, a, s);
+    case 3: return launch_rtn_bits<3>(p, grid, a, s);
+    default: return launch_rtn_bits<4>(p, grid, a, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace lbq

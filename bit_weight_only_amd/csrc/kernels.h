@@ -66,6 +66,9 @@ struct GemmPlan {
 };
 GemmPlan gemm_plan(int M, int K, int N);
 GemmPlan gemm_rtn_plan(int M, int K, int N);
+// longest K slice (groups) whose scale/zero words the RTN GEMM stages in LDS,
+// for nb row blocks per wave; launch_gemm_rtn rejects plans with longer slices
+int gemm_rtn_meta_max_groups(int nb);
 size_t gemm_scratch_bytes(const GemmPlan &p);
 int gemm_counters(const GemmPlan &p);
 uint32_t *gemm_counter_ptr(const GemmPlan &p, void *scratch);
