@@ -313,23 +313,32 @@ GemmPlan gemm_plan(int M, int K, int N) {
 
 GemmPlan gemm_rtn_plan(int M, int K, int N) {
   // Measured on the dense-stack and FFN shapes (K up to 17408, N 4096..28672,
-  // M 8..256): two row blocks per wave (each activation fragment read from LDS
-  // feeds two MFMAs), four once that alone gives >= 384 workgroups. Split K
-  // only until 128 workgroups run (256 for rows of >= 64 groups or for >= 128
-  // tokens, 512 for both), every slice keeping at least eight groups: split-K
-  // partial tiles go through device-coherent memory and cost more than a
-  // partly idle chip.
+  // M 8..256). Up to 32 tokens the loop is bound by each compute unit's
+  // vector-memory address path: one row block per wave, and K split until
+  // about 384 workgroups run, every slice keeping at least eight groups. From
+  // 33 tokens two row blocks per wave (each activation fragment read from LDS
+  // feeds two MFMAs), four once that alone gives >= 384 workgroups, and K split
+  // until 256 workgroups run (512 for rows of >= 64 groups at >= 128 tokens),
+  // slices of at least sixteen groups: split-K partial tiles go through
+  // device-coherent memory and cost more than a partly idle chip.
   GemmPlan p;
   p.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   const int G = K / kGroup;
   p.m_tiles = M > 0 ? (M + 16 * p.mt - 1) / (16 * p.mt) : 0;
-  const long t4 = static_cast<long>((N + 255) / 256) * p.m_tiles;
-  p.nb = t4 >= 384 ? 4 : 2;
-  p.n_tiles = (N + 64 * p.nb - 1) / (64 * p.nb);
-  const long tiles = static_cast<long>(p.n_tiles) * p.m_tiles;
-  const long target = 128L << ((G >= 64 ? 1 : 0) + (M >= 128 ? 1 : 0));
   p.S = 1;
-  while (tiles * p.S < target && G / (2 * p.S) >= 8) p.S *= 2;
+  if (p.mt <= 2) {
+    p.nb = 1;
+    p.n_tiles = (N + 63) / 64;
+    const long tiles = static_cast<long>(p.n_tiles) * p.m_tiles;
+    while (tiles * p.S < 384 && G / (2 * p.S) >= 4) p.S *= 2;
+  } else {
+    const long t4 = static_cast<long>((N + 255) / 256) * p.m_tiles;
+    p.nb = t4 >= 384 ? 4 : 2;
+    p.n_tiles = (N + 64 * p.nb - 1) / (64 * p.nb);
+    const long tiles = static_cast<long>(p.n_tiles) * p.m_tiles;
+    const long target = (G >= 64 && M >= 128) ? 512 : 256;
+    while (tiles * p.S < target && G / (2 * p.S) >= 8) p.S *= 2;
+  }
   // slices short enough for the kernel to stage their scale/zero words in LDS
   while ((G + p.S - 1) / p.S > gemm_rtn_meta_max_groups(p.nb)) p.S *= 2;
   return p;
