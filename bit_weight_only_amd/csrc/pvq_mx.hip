@@ -28,6 +28,11 @@ using namespace mx;
 
 constexpr int kPvqMaxThreads = 1024;
 constexpr int kGB = 2;   // groups per item: 64 index bytes of a row, 16 bytes per lane
+// The codebook table in LDS is replicated: entry e of copy c at word 32 e + c,
+// and lane l reads copy l & 31. The 32 lanes of one LDS pass then hit 32
+// distinct banks whatever their indices (one table: random indices collide
+// several ways per pass, and every weight quad is one lookup).
+constexpr int kLutCopies = 32;
 
 // Rotate one unit and write its A pieces in the product-VQ element order:
 // positions 16 L + 4 w .. 16 L + 4 w + 3 are word 8 (L & 3) + 4 (L >> 2) + w of
@@ -69,11 +74,12 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
   const int nw = static_cast<int>(blockDim.x >> 6), nt = static_cast<int>(blockDim.x);
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));   // wave-uniform
   const int lane = static_cast<int>(threadIdx.x & 63), j = lane & 15, kq = lane >> 4;
+  const uint32_t lcopy = static_cast<uint32_t>(lane) & (kLutCopies - 1);   // this lane's codebook copy
 
-  // LDS: codebook [256] words, piece sets [M][Gp], A-scale exponents [M][Gp],
-  // the waves' row partial sums [nw][M][rows].
+  // LDS: codebook [256][kLutCopies] words, piece sets [M][Gp], A-scale
+  // exponents [M][Gp], the waves' row partial sums [nw][M][rows].
   uint32_t *lut = smem;
-  uint32_t *xa = smem + 256;
+  uint32_t *xa = smem + 256 * kLutCopies;
   uint32_t *sx = xa + M * Gp * (kSetBytes / 4);
   float *yl = reinterpret_cast<float *>(sx + M * Gp);
 
@@ -146,7 +152,11 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (threadIdx.x < 256) lut[threadIdx.x] = cw;
+  {   // thread t writes copies [cpt (t >> 8), cpt (t >> 8) + cpt) of entry t & 255
+    const int cpt = 256 * kLutCopies / nt, c0 = (static_cast<int>(threadIdx.x) >> 8) * cpt;
+    uint32_t *dst = lut + (threadIdx.x & 255) * kLutCopies + c0;
+    for (int c = 0; c < cpt; c += 4) *reinterpret_cast<uint4 *>(dst + c) = make_uint4(cw, cw, cw, cw);
+  }
   {   // every set's zero piece, the row sums
     for (int i = static_cast<int>(threadIdx.x); i < M * G * (kPieceBytes / 16); i += nt) {
       const int q = i / (kPieceBytes / 16);
@@ -180,7 +190,8 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bv[4 * h + i] = static_cast<int>(lut[(w[2 * u + h] >> (8 * i)) & 0xFFu]);
+        for (int i = 0; i < 4; ++i)
+          bv[4 * h + i] = static_cast<int>(lut[(((w[2 * u + h] >> (8 * i)) & 0xFFu) * kLutCopies) | lcopy]);
       const uint4 *ap4 = reinterpret_cast<const uint4 *>(lds + a_base + (g0 + u) * kSetBytes);
       const uint4 x0 = ap4[0], x1 = ap4[1];
       const v8i_t av = {static_cast<int>(x0.x), static_cast<int>(x0.y), static_cast<int>(x0.z),
@@ -218,7 +229,7 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
 }
 
 size_t pvq_mx_lds(int M, int G, int rows, int block) {
-  return 1024 + static_cast<size_t>(M) * G * (kSetBytes + 4) + static_cast<size_t>(block / 64) * M * rows * 4;
+  return 1024 * kLutCopies + static_cast<size_t>(M) * G * (kSetBytes + 4) + static_cast<size_t>(block / 64) * M * rows * 4;
 }
 
 constexpr int kComputeUnits = 256;
