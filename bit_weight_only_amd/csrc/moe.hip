@@ -3,11 +3,11 @@
 // in a Hadamard-rotated basis: LLaDA2.2-mini Orin Nano card, "Routed Experts").
 //
 // Passes, all on the caller's stream:
-//   1. route:   one workgroup; per token (a wavefront each) the top_k logits
-//               (ties to the lower expert id) and softmax weights over them;
-//               per-expert counts, exclusive offsets, and the assignment list
-//               grouped by expert (a counting sort over token chunks, one
-//               wavefront per chunk).
+//   1. route:   per pair of tokens (a workgroup of one wavefront each) the
+//               top_k logits (ties to the lower expert id) and softmax weights
+//               over them; then, in one workgroup, per-expert counts, exclusive
+//               offsets, and the assignment list grouped by expert (a counting
+//               sort over token chunks, one wavefront per chunk).
 //   2. rotate:  x' = R_hidden x once per token (the rotate kernel).
 //   3. gate|up: one workgroup per (expert, 128-wide block of the ffn axis);
 //               inactive experts exit at once. It decodes the 128 gate rows and
@@ -67,18 +67,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
+// The router runs as two launches. Its top-k rounds are chains of dependent
+// lane exchanges; on one workgroup the waves of all tokens shared one compute
+// unit's issue slots (about 7 us for 32 tokens), so the top-k launch spreads
+// the token pairs over workgroups of one wavefront each, and a one-workgroup
+// launch then sorts the assignments.
+
 // PER: experts per lane (E <= 64 PER).
 template <int PER>
-__global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *__restrict__ logits, int M, int E,
-                                                                  int top_k, int32_t *__restrict__ ids,
-                                                                  float *__restrict__ weights,
-                                                                  int32_t *__restrict__ counts,
-                                                                  int32_t *__restrict__ offsets,
-                                                                  int32_t *__restrict__ perm) {
-  constexpr int kWaves = kRouteThreads / 64;
-  __shared__ int32_t s_ids[kMaxAssignments];
-  __shared__ int32_t s_cnt[kWaves * kMaxExperts];   // per (token chunk, expert): count, then run start
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ void __launch_bounds__(64) moe_topk_kernel(const float *__restrict__ logits, int M, int E, int top_k,
+                                                      int32_t *__restrict__ ids, float *__restrict__ weights) {
+  const int lane = threadIdx.x & 63;
 
   // 1. top-k per token, one wavefront per pair of tokens (their dependent
   //    chains interleave). Expert e = lane + 64 i holds the order key of its
@@ -87,7 +86,7 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
   //    and, among the experts holding it, the lowest id (ties go to the lower
   //    id), and clears it. A pair's second token past M computes on copies of
   //    the first and stores nothing.
-  for (int t0 = 2 * wave; t0 < M; t0 += 2 * kWaves) {
+  for (int t0 = 2 * static_cast<int>(blockIdx.x); t0 < M; t0 += 2 * static_cast<int>(gridDim.x)) {
     const int tt[2] = {t0, min(t0 + 1, M - 1)};
     const bool ok1 = t0 + 1 < M;
     // all loads first, unconditionally at clamped indices, then the keys
@@ -128,7 +127,7 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
         const float v = float_unorder(best[p]);
         if (r == 0) sel0[p] = v;
         if (lane == r) mine[p] = v;
-        if (lane == 0 && (p == 0 || ok1)) s_ids[tt[p] * top_k + r] = e;
+        if (lane == 0 && (p == 0 || ok1)) ids[tt[p] * top_k + r] = e;
       }
     }
     // softmax over the selected logits (shifted by the largest)
@@ -144,6 +143,16 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
       if (lane < top_k && (p == 0 || ok1)) weights[tt[p] * top_k + lane] = ex / denom;
     }
   }
+}
+
+__global__ void __launch_bounds__(kRouteThreads) moe_sort_kernel(const int32_t *__restrict__ ids, int M, int E,
+                                                                  int top_k, int32_t *__restrict__ counts,
+                                                                  int32_t *__restrict__ offsets,
+                                                                  int32_t *__restrict__ perm) {
+  constexpr int kWaves = kRouteThreads / 64;
+  __shared__ int32_t s_ids[kMaxAssignments];
+  __shared__ int32_t s_cnt[kWaves * kMaxExperts];   // per (token chunk, expert): count, then run start
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // 2. counting sort of the assignments by expert, stable in the assignment
   //    index. Wave w owns the contiguous token chunk [w C, (w + 1) C); a
   //    token's top_k experts are distinct, so the lanes of one token never
@@ -154,8 +163,8 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const float *_
   const int chunk = (M + kWaves - 1) / kWaves;
   const int t_lo = min(M, wave * chunk), t_hi = min(M, t_lo + chunk);
   for (int i = threadIdx.x; i < kWaves * E; i += kRouteThreads) s_cnt[i] = 0;
+  for (int a = threadIdx.x; a < MK; a += kRouteThreads) s_ids[a] = ids[a];
   __syncthreads();
-  for (int a = threadIdx.x; a < MK; a += kRouteThreads) ids[a] = s_ids[a];
   for (int t = t_lo; t < t_hi; ++t)
     if (lane < top_k) s_cnt[wave * E + s_ids[t * top_k + lane]] += 1;
   __syncthreads();
@@ -404,10 +413,10 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const float *__restric
 
 hipError_t launch_moe_route(const float *logits, int M, int E, int top_k, int32_t *ids, float *weights,
                             int32_t *counts, int32_t *offsets, int32_t *perm, hipStream_t s) {
-  auto kern = E <= 64 ? moe_route_kernel<1> : E <= 256 ? moe_route_kernel<4> : E <= 512 ? moe_route_kernel<8>
-                                                                                  : moe_route_kernel<16>;
-  hipLaunchKernelGGL(kern, dim3(1), dim3(kRouteThreads), 0, s, logits, M, E, top_k, ids, weights, counts, offsets,
-                     perm);
+  auto topk = E <= 64 ? moe_topk_kernel<1> : E <= 256 ? moe_topk_kernel<4> : E <= 512 ? moe_topk_kernel<8>
+                                                                                : moe_topk_kernel<16>;
+  if (M > 0) hipLaunchKernelGGL(topk, dim3(static_cast<unsigned>((M + 1) / 2)), dim3(64), 0, s, logits, M, E, top_k, ids, weights);
+  hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, M, E, top_k, counts, offsets, perm);
   return hipGetLastError();
 }
 
