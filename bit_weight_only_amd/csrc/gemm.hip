@@ -317,7 +317,8 @@ GemmPlan gemm_rtn_plan(int M, int K, int N) {
   // vector-memory address path: one row block per wave, and K split until
   // about 384 workgroups run, every slice keeping at least eight groups. From
   // 33 tokens two row blocks per wave (each activation fragment read from LDS
-  // feeds two MFMAs), four once that alone gives >= 384 workgroups, and K split
+  // feeds two MFMAs; one for rows of >= 64 groups below 128 tokens), four once
+  // that alone gives >= 384 workgroups, and K split
   // until 256 workgroups run (512 for rows of >= 64 groups at >= 128 tokens),
   // slices of at least sixteen groups: split-K partial tiles go through
   // device-coherent memory and cost more than a partly idle chip.
@@ -333,7 +334,8 @@ GemmPlan gemm_rtn_plan(int M, int K, int N) {
     while (tiles * p.S < 384 && G / (2 * p.S) >= 4) p.S *= 2;
   } else {
     const long t4 = static_cast<long>((N + 255) / 256) * p.m_tiles;
-    p.nb = t4 >= 384 ? 4 : 2;
+    // long rows below 128 tokens: one block per wave, the split carries the chip
+    p.nb = t4 >= 384 ? 4 : (G >= 64 && M < 128) ? 1 : 2;
     p.n_tiles = (N + 64 * p.nb - 1) / (64 * p.nb);
     const long tiles = static_cast<long>(p.n_tiles) * p.m_tiles;
     const long target = (G >= 64 && M >= 128) ? 512 : 256;
