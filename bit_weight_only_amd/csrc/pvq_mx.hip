@@ -4,8 +4,9 @@
 //
 // v_mfma_scale_f32_16x16x128_f8f6f4 with both operands e4m3:
 //  * B = codebook values. An index byte picks four e4m3 values for four
-//    consecutive weights: one 32-bit word of the B operand, read from a 1 KB
-//    table in LDS. Lane (j, kq) of a group takes the index bytes 4 kq .. 4 kq + 3
+//    consecutive weights: one 32-bit word of the B operand, read from a table
+//    in LDS (32 copies of the 1 KB codebook, one per lane of an LDS pass).
+//    Lane (j, kq) of a group takes the index bytes 4 kq .. 4 kq + 3
 //    and 16 + 4 kq .. 16 + 4 kq + 3 of row j's 32 (weights 16 kq .. 16 kq + 15
 //    and 64 + 16 kq .. 64 + 16 kq + 15), the word columns a 4x4 lane transpose
 //    of the row's 16-byte loads hands it.
