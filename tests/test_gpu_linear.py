@@ -99,6 +99,21 @@ def test_gemv_matrix_core_tokens(L, dev, bits, n, k, m):
     assert O.rel_l2(y[:, rows], want) < TOL
 
 
+@pytest.mark.parametrize("m", [1, 2])
+def test_gemv_matrix_core_tall_4bit(L, dev, m):
+    """Tall 4-bit matrices with small rotations launch two 512-thread
+    workgroups per compute unit (1025 row tiles here, a ragged last one);
+    sampled rows against the oracle, both ends included."""
+    n, k, bits = 16400, 1024, 4
+    say(f"gemv mfma tall 4-bit n={n} k={k} m={m}")
+    w, s, planes, meta, pl = make_rtn(n, k, bits, 18, m)
+    x = synth.activations(m, k, workload=18, item=m)
+    y = L.linear_forward(pl, to_dev(x, dev)).cpu().numpy().astype(np.float64)
+    rows = sample_rows(n, 64, seed=m)
+    want = oracle_rtn_rows(w, s, bits, x, rows)
+    assert O.rel_l2(y[:, rows], want) < TOL
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("n,k", [(257, 4096), (130, 5120), (67, 8192)])
 @pytest.mark.parametrize("m", [1, 2])
