@@ -238,3 +238,26 @@ def test_rotate_and_unpack_argument_errors(L):
     w = _w(L)
     assert lib.lbq_unpack_codes(ctypes.byref(w), 0, None) == -1
     assert lib.lbq_unpack_codes(ctypes.byref(w), FAKE + 1, None) == -4
+
+
+def test_host_pack_matches_hand_derived_groups(L, golden_dir):
+    """The library's packer on the hand-derived groups of rtn_spikes.json
+    (spikes, and one-signed groups whose range must include 0)."""
+    import json
+    import math
+
+    import scipy.linalg
+
+    with open(os.path.join(golden_dir, "rtn_spikes.json")) as f:
+        g = json.load(f)
+    h = scipy.linalg.hadamard(128).astype(np.float64)
+    for c in g["cases"]:
+        k = c["K"]
+        wv = np.zeros(k)
+        for i, a in c["spikes"]:
+            wv += a / math.sqrt(128.0) * h[:, i]
+        wv[0] += c.get("offset", 0.0) * math.sqrt(128.0)
+        planes, meta = L.pack(wv.astype(np.float32)[None, :], c["bits"], np.ones(k, np.int8))
+        assert np.array_equal(planes.view(np.uint32).reshape(c["bits"], 4), np.array(c["planes"], np.uint32)), c["name"]
+        sz = meta.view(np.uint16)
+        assert int(sz[0]) == c["scale_bits"] and int(sz[1]) == c["zero_bits"], c["name"]

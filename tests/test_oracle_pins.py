@@ -228,6 +228,7 @@ def test_rtn_spike_fixtures(golden_dir):
         wv = np.zeros(k)
         for i, a in c["spikes"]:
             wv += a / math.sqrt(128.0) * h[:, i]
+        wv[0] += c.get("offset", 0.0) * math.sqrt(128.0)   # the same b in every rotated value
         w = wv.astype(np.float32)[None, :]
         planes, meta, q = O.pack_rtn(w, c["bits"], np.ones(k, np.int8))
         want = np.full(k, c["default_code"], dtype=np.uint8)
@@ -433,3 +434,25 @@ def test_pvq_linear_matches_explicit_gather():
             wq[i, kk] = float(sc.view(np.float16)[i]) * c[idx[i, kk // 4], kk % 4]
     np.testing.assert_allclose(y, x.astype(np.float64) @ (wq @ r).T, rtol=1e-12, atol=1e-14)
     assert O.rel_l2(y, x.astype(np.float64) @ w.astype(np.float64).T) < 0.6
+
+
+# ---------------------------------------------------------------- parity metric
+
+def test_rel_l2_hand_values():
+    """The parity gate: ||a - b||_2 / ||b||_2 over the whole array, b the
+    reference (values worked out by hand; a slip such as dividing by ||b||^2,
+    by ||a||, or averaging per row fails one of these)."""
+    b = np.array([6.0, 8.0])                    # ||b|| = 10
+    a = b + np.array([3.0, 4.0])                # ||a - b|| = 5, ||a|| = 15
+    assert O.rel_l2(a, b) == 0.5
+    assert O.rel_l2(b, a) == 5.0 / 15.0         # the second argument is the reference
+    # whole-array norm, not a mean of per-row ratios: rows (0.1, 1.0) would average 0.55
+    ref = np.array([[10.0, 0.0], [0.0, 1.0]])
+    got = ref + np.array([[1.0, 0.0], [0.0, 1.0]])
+    assert O.rel_l2(got, ref) == np.sqrt(2.0) / np.sqrt(101.0)
+    assert O.rel_l2(ref, ref) == 0.0
+    # a zero reference has no relative error: the absolute norm is returned
+    assert O.rel_l2(np.array([3.0, 4.0]), np.zeros(2)) == 5.0
+    assert O.rel_l2(np.zeros(3), np.zeros(3)) == 0.0
+    # fp16 inputs are widened exactly before the norms
+    assert O.rel_l2(np.array([1.0, 2.0], np.float16), np.array([1.0, 1.0], np.float16)) == 1.0 / np.sqrt(2.0)
