@@ -53,6 +53,9 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
   lbq_status st = check_weight(w);
   if (st != LBQ_OK) return st;
   if (M < 0) return LBQ_ERR_SHAPE;
+  // test flag: the GEMM's rotation in launches of at most three tokens
+  const int rot_tokens = (path & LBQ_PATH_SPLIT_ROTATION) ? 3 : 0;
+  path &= ~LBQ_PATH_SPLIT_ROTATION;
   if (path < LBQ_PATH_AUTO || path > LBQ_PATH_GEMM) return LBQ_ERR_SHAPE;
   if (path == LBQ_PATH_GEMV && M > 16) return LBQ_ERR_SHAPE;
   if (M == 0) return LBQ_OK;
@@ -84,8 +87,8 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
     uint8_t *after_x = static_cast<uint8_t *>(ws) + round_up(static_cast<size_t>(M) * w->K * 2, kAlign);
     uint32_t *tz = rtn ? reinterpret_cast<uint32_t *>(after_x) : nullptr;
     void *scratch = after_x + tz_bytes(w, M);
-    if (launch_rotate_folded(x, M, w->K, w->signs, xr, tz, gemm_counter_ptr(gp, scratch), gemm_counters(gp), s) !=
-        hipSuccess)
+    if (launch_rotate_folded(x, M, w->K, w->signs, xr, tz, gemm_counter_ptr(gp, scratch), gemm_counters(gp), s,
+                             rot_tokens) != hipSuccess)
       return LBQ_ERR_HIP;
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return LBQ_ERR_HIP;
     const hipError_t ge =

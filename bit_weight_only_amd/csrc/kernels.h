@@ -13,24 +13,14 @@ hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, u
 // Rotation into the folded slot order (u32 slot c of each 32-chunk holds
 // (x'[c], x'[c+16])); with tz non-null also the RTN GEMM's per-(token, group)
 // sums tz[m * gemm_tz_stride(K) + g] = (T/16 high, T/16 low) fp16, zero-padded;
-// also zeroes n_counters u32 at counters.
+// also zeroes n_counters u32 at counters. The tokens go in launches of under
+// 1 GiB of activations, or of max_tokens tokens when max_tokens > 0 is lower.
 hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, uint32_t *tz,
-                                uint32_t *counters, int n_counters, hipStream_t s);
+                                uint32_t *counters, int n_counters, hipStream_t s, int max_tokens = 0);
 
 // RTN dequant-GEMV for 1 <= M <= 16 on already-rotated activations xr [M][K].
 hipError_t launch_gemv_rtn(const void *planes, const void *meta, const uint16_t *xr, uint16_t *y, int M, int K,
                            int N, int bits, hipStream_t s);
-
-// RTN dequant-GEMV on raw activations x [M][K] (M = 1 or 2) with the rotation
-// in the kernel's prologue: one launch, no workspace. signs must be 16-byte
-// aligned. gemv_fold_supported says where this path is the faster one;
-// lanes <= 0 picks the launch shape (gemv_fold_shape). Non-null events take
-// the kernel's own begin / end times (hipExtLaunchKernel).
-bool gemv_fold_supported(int M, int K);
-void gemv_fold_shape(int M, int K, int N, int &lanes, int &rb, int &grid_cap);
-hipError_t launch_gemv_fold(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs, uint16_t *y,
-                            int M, int K, int N, int bits, int lanes, int rb, int grid_cap, hipStream_t s,
-                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // RTN dequant-GEMV on raw activations x [M][K] (1 <= M <= 4) on the matrix
 // cores (fp8 activation pieces x fp4 code operands), rotation fused into the

@@ -138,12 +138,13 @@ __global__ void __launch_bounds__(256) rotate_folded_kernel(const uint32_t *__re
 }
 
 hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, uint32_t *tz,
-                                uint32_t *counters, int n_counters, hipStream_t s) {
+                                uint32_t *counters, int n_counters, hipStream_t s, int max_tokens) {
   // 32 (token, group) units per workgroup; buffer offsets are 32-bit, so the
   // tokens go in launches of under 1 GiB of activations each (the first also
-  // clears the counters)
+  // clears the counters); max_tokens > 0 caps a launch lower
   const int Gp = gemm_tz_stride(K);
-  const int per = std::max(1, static_cast<int>((1L << 30) / (static_cast<long>(K) * 2)));
+  int per = std::max(1, static_cast<int>((1L << 30) / (static_cast<long>(K) * 2)));
+  if (max_tokens > 0 && max_tokens < per) per = max_tokens;
   int m0 = 0;
   do {
     const int Mc = std::min(per, M - m0);

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "liblbq.so")
 FMT_RTN_PLANES = 0
 FMT_PVQ_4x8 = 1
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+PATH_SPLIT_ROTATION = 0x100   # test flag: the GEMM's rotation in launches of <= 3 tokens
 
 STATUS = {
     0: "LBQ_OK", -1: "LBQ_ERR_NULL", -2: "LBQ_ERR_SHAPE", -3: "LBQ_ERR_BITS", -4: "LBQ_ERR_ALIGN",

@@ -80,11 +80,15 @@ typedef enum {
 } lbq_format;
 
 /* Kernel path for lbq_linear_forward_path. AUTO picks the GEMV for M <= 4 and
- * the MFMA GEMM above (measured crossover); forcing the GEMV needs M <= 16. */
+ * the MFMA GEMM above (measured crossover); forcing the GEMV needs M <= 16.
+ * LBQ_PATH_SPLIT_ROTATION may be OR-ed into any of them (for tests): the
+ * GEMM's separate rotation launch then goes in launches of at most three
+ * tokens each, the split it otherwise makes only past 1 GiB of activations. */
 typedef enum {
   LBQ_PATH_AUTO = 0,
   LBQ_PATH_GEMV = 1,
-  LBQ_PATH_GEMM = 2
+  LBQ_PATH_GEMM = 2,
+  LBQ_PATH_SPLIT_ROTATION = 0x100
 } lbq_path;
 
 /* A packed weight: a plain view of caller-owned device buffers. */
@@ -116,14 +120,27 @@ typedef struct {
   const int8_t *signs_ffn;        /* [ffn] */
 } lbq_moe;
 
-/* Text for a status code (static storage). */
+/* Text for a status code (static storage; never NULL, unknown codes give
+ * "unknown status"). */
 const char *lbq_status_string(lbq_status s);
 
-/* Byte sizes of the packed buffers of one K x N weight (host query). */
+/* Byte sizes of the packed buffers of one K x N weight (host query; nothing
+ * is launched). RTN: planes N*K*bits/8, meta 4*N*K/128 (the bit-plane layout
+ * above: Qwen3-8B BPDQ card, opening paragraph; the fp16 scale and zero per
+ * 128-group: LLaDA2.2-mini card, "Routed Experts" row). PVQ: indices N*K/4,
+ * row scales 2*N (Laguna-S-2.1 card, opening paragraph: two 8-bit indices per
+ * 8-weight vector). Errors: LBQ_ERR_NULL (an output pointer), LBQ_ERR_BITS,
+ * LBQ_ERR_FORMAT, LBQ_ERR_SHAPE. */
 lbq_status lbq_packed_bytes(int32_t K, int32_t N, int32_t bits, int32_t format,
                             size_t *plane_bytes, size_t *meta_bytes);
 
-/* Offline packing on the host (threaded, float64 arithmetic):
+/* Offline packing on the host (threaded, float64 arithmetic). The method
+ * quantizes each weight in a Hadamard-rotated basis with group-128 codes and
+ * stores the rotation signs beside it (LLaDA2.2-mini card, property table,
+ * "Routed Experts" row, and its file list), as bit-planes (Qwen3-8B BPDQ card,
+ * opening paragraph) or as product-VQ indices into an fp8-valued codebook
+ * (Laguna-S-2.1 card, opening paragraph). All buffers are host memory owned by
+ * the caller; nothing is launched.
  *   W: host fp32 [N][K] row-major (PyTorch Linear layout, y = x W^T).
  *   signs: host int8 [K] of +-1.  codebook: host [256][4] e4m3 bytes (PVQ only).
  *   planes_out / meta_out: host buffers of lbq_packed_bytes' sizes.
@@ -141,50 +158,76 @@ lbq_status lbq_pack(const float *W, int32_t K, int32_t N, int32_t bits, int32_t 
                     const int8_t *signs, const uint8_t *codebook,
                     void *planes_out, void *meta_out);
 
-/* Workspace bytes lbq_linear_forward needs for M tokens (host query). */
+/* Workspace bytes lbq_linear_forward needs for M tokens (host query; the
+ * rotated activations, the GEMM's zero-point sums and its split-K partial
+ * tiles and counters). Errors as lbq_linear_forward's argument checks. */
 lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
 
-/* y[M][N] (fp16) = x[M][K] (fp16) W_hat^T, W_hat the weight w decodes to.
- * The activation rotation runs either inside the GEMV's prologue (RTN codes,
- * signs 16-byte aligned: one to four tokens on the matrix cores when K is a
- * multiple of 512, else one or two tokens on rows of up to 8192 / 4096 inputs)
- * or as its own launch into the workspace, followed by the dequant-GEMV
- * (M <= 4) or the MFMA dequant-GEMM (M >= 5). Accumulation is fp32; the
- * GEMM rounds each decoded RTN weight s q to fp16 (the zero-point term s z
- * sum_k x'_k is added separately). The RTN GEMM needs N*K*b/8 < 2^31 - 4096
- * (LBQ_ERR_SHAPE otherwise). The result of a call does not depend on timing:
- * repeat calls give identical bits. */
+/* y[M][N] (fp16) = x[M][K] (fp16) W_hat^T, W_hat the weight w decodes to:
+ * the weight stays packed and is decoded inside the matmul (Qwen3-8B BPDQ
+ * card, opening paragraph: bit-planes kept packed for the whole run;
+ * Laguna-S-2.1 card, opening paragraph: codebook decode at matmul time), the
+ * activations are rotated into the weight's basis (Qwen3.8-27B Pingala-8 card,
+ * "What this is": random Hadamard rotation).
+ *   x: fp16 [M][K], y: fp16 [M][N], row-major, device, 16-byte aligned;
+ *   ws: device workspace of lbq_linear_workspace(w, M) bytes or more.
+ * Paths (AUTO):
+ *   - M <= 4, K a multiple of 512, signs 16-byte aligned (PVQ: codebook 4-byte
+ *     aligned): one launch, the matrix-core GEMV with the rotation in its
+ *     prologue (nothing is written to ws);
+ *   - other M <= 4: a rotation launch into ws, then the staged VALU GEMV;
+ *   - M >= 5: a rotation launch into ws (folded order, with the RTN
+ *     zero-point sums), then the MFMA dequant-GEMM.
+ * Accumulation is fp32; the GEMM rounds each decoded RTN weight s q to fp16
+ * (the zero-point term s z sum_k x'_k is added separately). The RTN GEMM needs
+ * N*K*b/8 < 2^31 - 4096 (LBQ_ERR_SHAPE otherwise). The result of a call does
+ * not depend on timing: repeat calls give identical bits. Errors are returned
+ * before any launch: LBQ_ERR_NULL, _SHAPE, _BITS, _ALIGN, _FORMAT, _WORKSPACE;
+ * LBQ_ERR_HIP if a launch fails. */
 lbq_status lbq_linear_forward(const lbq_weight *w, const uint16_t *x, int32_t M,
                               uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 
-/* lbq_linear_forward with an explicit kernel path (lbq_path). */
+/* lbq_linear_forward with an explicit kernel path (lbq_path, optionally with
+ * LBQ_PATH_SPLIT_ROTATION): LBQ_PATH_GEMV (M <= 16, LBQ_ERR_SHAPE above) or
+ * LBQ_PATH_GEMM (any M). The same operation and arguments; for tests that
+ * reach every kernel at shapes AUTO would send elsewhere. */
 lbq_status lbq_linear_forward_path(const lbq_weight *w, const uint16_t *x, int32_t M,
                                    uint16_t *y, void *ws, size_t ws_bytes, int32_t path,
                                    void *stream);
 
 /* lbq_linear_forward (AUTO path) with the main kernel's duration bracketed by
  * two caller-owned HIP events (hipEvent_t created with timing enabled; either
- * may be NULL). For the single-token GEMV with the rotation in its prologue
- * the events take that kernel's own begin and end times (hipExtLaunchKernel);
- * on the other paths they are recorded on the stream right before and after
- * the GEMV / GEMM launch (after the separate rotation launch). For measuring
- * the kernel; the result is the one lbq_linear_forward gives. */
+ * may be NULL), for measuring the decode kernel against the bytes it moves
+ * (Laguna-S-2.1 card, "Reading it honestly": decode speed tracks bytes). For
+ * the RTN matrix-core GEMV (rotation in its prologue) the events take that
+ * kernel's own begin and end times (hipExtLaunchKernel); on the other paths
+ * they are recorded on the stream right before and after the GEMV / GEMM
+ * launch (after the separate rotation launch). The result is the one
+ * lbq_linear_forward gives. */
 lbq_status lbq_linear_forward_timed(const lbq_weight *w, const uint16_t *x, int32_t M,
                                     uint16_t *y, void *ws, size_t ws_bytes, void *stream,
                                     void *start_event, void *stop_event);
 
-/* Workspace bytes lbq_moe_forward needs for M tokens (host query). */
+/* Workspace bytes lbq_moe_forward needs for M tokens (host query): router
+ * outputs, the per-assignment intermediates and expert outputs. */
 lbq_status lbq_moe_workspace(const lbq_moe *m, int32_t M, size_t *bytes);
 
-/* Routed-expert MoE block: per token t, the top_k experts by logit (ties to the
- * lower id) with softmax weights over the selected logits; for each selected
- * expert e: h = x_t W_gu(e)^T, a = silu(h[:ffn]) * h[ffn:], o = a W_dn(e)^T;
+/* Routed-expert MoE block (Laguna-S-2.1 card, base-model line: routed experts
+ * chosen top-k per token; LLaDA2.2-mini card, "Routed Experts" row: each expert
+ * at its own 2/3/4-bit width, group-128 codes in the rotated basis): per
+ * token t, the top_k experts by logit (ties to the lower id) with softmax
+ * weights over the selected logits; for each selected expert e:
+ * h = x_t W_gu(e)^T, a = silu(h[:ffn]) * h[ffn:], o = a W_dn(e)^T;
  * y_t = sum_j w_tj o_tj, summed in fp32 in slot order, written fp16.
- *   x: fp16 [M][hidden]; logits: fp32 [M][E]; y: fp16 [M][hidden]. */
+ *   x: fp16 [M][hidden]; logits: fp32 [M][E]; y: fp16 [M][hidden] (device,
+ *   16-byte aligned); ws: lbq_moe_workspace(m, M) bytes.
+ * Limits: E <= 1024, top_k <= 32, M * top_k <= 8192 (LBQ_ERR_SHAPE). Errors
+ * as lbq_linear_forward. */
 lbq_status lbq_moe_forward(const lbq_moe *m, const uint16_t *x, const float *logits, int32_t M,
                            uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 
-/* Router pass alone (the first step of lbq_moe_forward), for inspection:
+/* Router pass alone (the first step of lbq_moe_forward; Laguna-S-2.1 card,
+ * base-model line: 256 routed experts, top-k per token), for inspection:
  *   ids int32 [M][top_k], weights fp32 [M][top_k], counts int32 [E],
  *   offsets int32 [E+1] (exclusive prefix sum of counts), perm int32 [M*top_k]
  *   = assignment indices t*top_k + j grouped by expert in offset order and, within
@@ -193,11 +236,17 @@ lbq_status lbq_moe_route(const float *logits, int32_t M, int32_t E, int32_t top_
                          int32_t *ids, float *weights, int32_t *counts, int32_t *offsets,
                          int32_t *perm, void *stream);
 
-/* Codes as the GPU decoders see them: RTN writes uint8 codes [N][K] produced by
- * the kernels' own plane-merge routine; PVQ copies the uint8 indices [N][K/4]. */
+/* Codes as the GPU decoders see them, for the bit-exact read-back check
+ * (Qwen3.8-27B Pingala-8 card, "Results": the packed file read back tensor by
+ * tensor against freshly regenerated data with zero mismatches): RTN writes
+ * uint8 codes [N][K] produced by the kernels' own plane-merge routine; PVQ
+ * copies the uint8 indices [N][K/4]. codes: device, 16-byte aligned. */
 lbq_status lbq_unpack_codes(const lbq_weight *w, uint8_t *codes, void *stream);
 
-/* out[M][K] (fp16) = R x for each token row (fp32 butterflies, fp16 out). */
+/* out[M][K] (fp16) = R x for each token row, R = blockdiag(c H_128 diag(s))
+ * (Qwen3.8-27B Pingala-8 card, "What this is": random Hadamard rotation;
+ * LLaDA2.2-mini card, file list: stored rotation signs); fp32 butterflies,
+ * fp16 out. x, out: device [M][K], 16-byte aligned; signs: device [K]. */
 lbq_status lbq_rotate(const uint16_t *x, int32_t M, int32_t K, const int8_t *signs,
                       uint16_t *out, void *stream);
 
