@@ -2,7 +2,9 @@
 // and kernel launches on the caller's stream. No allocation, no global state.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/lbq.h"
 #include "kernels.h"
@@ -187,6 +189,66 @@ lbq_status lbq_linear_forward_timed(const lbq_weight *w, const uint16_t *x, int3
 lbq_status lbq_linear_forward(const lbq_weight *w, const uint16_t *x, int32_t M, uint16_t *y, void *ws,
                               size_t ws_bytes, void *stream) {
   return lbq_linear_forward_path(w, x, M, y, ws, ws_bytes, LBQ_PATH_AUTO, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation entry point
+
+namespace {
+
+// The workspace of lbq_linear_forward_noalloc: a file-scope device array, one
+// instance per GPU at that GPU's own address, held until the process ends. In
+// host code its name is only a stand-in for the symbol: kernels get the device
+// address that hipGetSymbolAddress returns for the GPU in use.
+constexpr size_t kScratchBytes = LBQ_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the GPU the stream runs on (the current GPU
+// for the null stream), looked up once per GPU with that GPU current.
+lbq_status scratch_on(hipStream_t s, void **out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return LBQ_ERR_HIP;
+  int dev = cur;
+  if (s != nullptr && hipStreamGetDevice(s, &dev) != hipSuccess) return LBQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LBQ_ERR_HIP;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (dev != cur && hipSetDevice(dev) != hipSuccess) return LBQ_ERR_HIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (dev != cur && hipSetDevice(cur) != hipSuccess) return LBQ_ERR_HIP;
+      if (e != hipSuccess || !p) return LBQ_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return LBQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lbq_status lbq_linear_forward_noalloc(const lbq_weight *w, const uint16_t *x, int32_t M, uint16_t *y, void *stream) {
+  lbq_status st = check_weight(w);
+  if (st != LBQ_OK) return st;
+  if (M < 0) return LBQ_ERR_SHAPE;
+  if (M == 0) return LBQ_OK;
+  if (linear_ws_bytes(w, M) > kScratchBytes) return LBQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void *ws = nullptr;
+  st = scratch_on(s, &ws);
+  if (st != LBQ_OK) return st;
+  // the rotation launch clears the split-K counters the GEMM finds in the
+  // array (with a kernel, so the call can be captured in a graph)
+  return forward_impl(w, x, M, y, ws, kScratchBytes, LBQ_PATH_AUTO, stream, nullptr, nullptr);
 }
 
 lbq_status lbq_unpack_codes(const lbq_weight *w, uint8_t *codes, void *stream) {

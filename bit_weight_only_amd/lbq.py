@@ -29,7 +29,7 @@ STATUS = {
 EXPORTS = [
     "lbq_status_string", "lbq_packed_bytes", "lbq_pack", "lbq_linear_workspace", "lbq_linear_forward",
     "lbq_linear_forward_path", "lbq_linear_forward_timed", "lbq_moe_workspace", "lbq_moe_forward", "lbq_moe_route", "lbq_unpack_codes",
-    "lbq_rotate",
+    "lbq_rotate", "lbq_linear_forward_noalloc",
 ]
 
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.lbq_moe_route.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
         L.lbq_unpack_codes.argtypes = [ctypes.POINTER(Weight), c_vp, c_vp]
         L.lbq_rotate.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]
+        L.lbq_linear_forward_noalloc.argtypes = [ctypes.POINTER(Weight), c_vp, c_i32, c_vp, c_vp]
         for name in EXPORTS:
             if name != "lbq_status_string":
                 getattr(L, name).restype = c_i32
@@ -175,6 +176,18 @@ def linear_forward(w: PackedLinear, x, y=None, ws=None, path: int = PATH_AUTO, s
     st = lib().lbq_linear_forward_path(ctypes.byref(w.struct), _ptr(x), M, _ptr(y), _ptr(ws), ws.numel(), int(path),
                                        _stream(stream))
     _check(st, "lbq_linear_forward")
+    return y
+
+
+def linear_forward_noalloc(w: PackedLinear, x, y=None, stream=None):
+    """lbq_linear_forward_noalloc: y = x W_hat^T with the library's static device scratch (no workspace)."""
+    import torch
+
+    M = int(x.shape[0])
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.float16, device=x.device)
+    _check(lib().lbq_linear_forward_noalloc(ctypes.byref(w.struct), _ptr(x), M, _ptr(y), _stream(stream)),
+           "lbq_linear_forward_noalloc")
     return y
 
 

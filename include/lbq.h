@@ -208,6 +208,25 @@ lbq_status lbq_linear_forward_timed(const lbq_weight *w, const uint16_t *x, int3
                                     uint16_t *y, void *ws, size_t ws_bytes, void *stream,
                                     void *start_event, void *stop_event);
 
+/* Bytes of the device scratch array behind lbq_linear_forward_noalloc. */
+#define LBQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* lbq_linear_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments and result as lbq_linear_forward
+ * with the AUTO path, but with the library's own scratch in place of the
+ * caller's workspace. The scratch is a static device array of
+ * LBQ_NOALLOC_SCRATCH_BYTES per GPU (each GPU the library runs on holds it
+ * from its first use until the process ends); the call allocates nothing and
+ * returns LBQ_ERR_WORKSPACE, before any launch, when lbq_linear_workspace(w, M)
+ * exceeds it. Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (the calls clear what must start at zero themselves):
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race on it and give wrong results. The stream's GPU is the one used (the
+ * current GPU for the null stream). */
+lbq_status lbq_linear_forward_noalloc(const lbq_weight *w, const uint16_t *x, int32_t M,
+                                      uint16_t *y, void *stream);
+
 /* Workspace bytes lbq_moe_forward needs for M tokens (host query): router
  * outputs, the per-assignment intermediates and expert outputs. */
 lbq_status lbq_moe_workspace(const lbq_moe *m, int32_t M, size_t *bytes);
