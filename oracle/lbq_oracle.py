@@ -348,21 +348,28 @@ def expert_ffn(x16: np.ndarray, w_gu: np.ndarray, w_dn: np.ndarray) -> np.ndarra
     return a @ np.asarray(w_dn, dtype=np.float64).T
 
 
-def moe_forward(x16: np.ndarray, logits: np.ndarray, top_k: int, expert_weights) -> np.ndarray:
+def moe_forward(x16: np.ndarray, logits: np.ndarray, top_k: int, expert_weights=None,
+                expert_outputs=None) -> np.ndarray:
     """y_t = sum_j w_tj * FFN_{ids[t,j]}(x_t), float64 [M][hidden].
 
     ``expert_weights(e)`` returns the original-basis (W_gu_hat [2F][H],
-    W_dn_hat [H][F]) of expert e; experts are visited one at a time.
+    W_dn_hat [H][F]) of expert e; experts are visited one at a time. Instead,
+    ``expert_outputs(e, rows)`` may return FFN_e of the tokens ``rows`` (the
+    same expert_ffn, computed elsewhere, e.g. expert by expert in parallel).
     """
     ids, wts = route(logits, top_k)
     m, h = np.asarray(x16).shape
     y = np.zeros((m, h), dtype=np.float64)
     for e in np.unique(ids):
-        w_gu, w_dn = expert_weights(int(e))
         rows, slots = np.nonzero(ids == e)
-        o = expert_ffn(np.asarray(x16)[rows], w_gu, w_dn)
+        if expert_outputs is not None:
+            o = expert_outputs(int(e), rows)
+        else:
+            w_gu, w_dn = expert_weights(int(e))
+            o = expert_ffn(np.asarray(x16)[rows], w_gu, w_dn)
         y[rows] += wts[rows, slots][:, None] * o
     return y
+
 
 
 def moe_forward_per_assignment(x16, logits, top_k, expert_weights) -> np.ndarray:

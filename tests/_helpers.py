@@ -2,6 +2,7 @@
 and compute the oracle's answer on the same inputs (sampled rows for large
 weights: rows of a linear are independent, so the oracle packs and decodes
 only those)."""
+import os
 import sys
 
 import numpy as np
@@ -13,8 +14,15 @@ TOL = 2e-3       # relative L2 bound on fp16 outputs (fp16 activations, fp32 acc
 
 
 def say(*a):
+    """Print a progress / result line; with LBQ_PARITY_LOG set, also append it
+    to that file (the measured errors of a GPU run, kept for the results table)."""
     print(*a, flush=True)
     sys.stdout.flush()
+    path = os.environ.get("LBQ_PARITY_LOG")
+    if path:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+        with open(path, "a") as f:
+            f.write(f"{test}\t{' '.join(str(x) for x in a)}\n")
 
 
 def cuda():

@@ -102,9 +102,9 @@ def test_gemv_matrix_core_tokens(L, dev, bits, n, k, m):
 @pytest.mark.parametrize("m", [1, 2])
 def test_gemv_matrix_core_tall_4bit(L, dev, m):
     """Tall 4-bit matrices with small rotations launch two 512-thread
-    workgroups per compute unit (1025 row tiles here, a ragged last one);
+    workgroups per compute unit (1025 row tiles here, the last one ragged: 16393 = 1024 * 16 + 9);
     sampled rows against the oracle, both ends included."""
-    n, k, bits = 16400, 1024, 4
+    n, k, bits = 16393, 1024, 4
     say(f"gemv mfma tall 4-bit n={n} k={k} m={m}")
     w, s, planes, meta, pl = make_rtn(n, k, bits, 18, m)
     x = synth.activations(m, k, workload=18, item=m)
