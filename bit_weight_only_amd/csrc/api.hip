@@ -263,6 +263,16 @@ lbq_status lbq_unpack_codes(const lbq_weight *w, uint8_t *codes, void *stream) {
                                    hipMemcpyDeviceToDevice, s));
 }
 
+lbq_status lbq_stream_read(const void *buf, size_t bytes, int32_t grid, int32_t block, uint32_t *sink,
+                           void *stream, void *start_event, void *stop_event) {
+  if (!sink || (bytes > 0 && !buf)) return LBQ_ERR_NULL;
+  if (bytes % 16 != 0 || bytes / 16 >= (static_cast<size_t>(1) << 32)) return LBQ_ERR_SHAPE;
+  if (grid < 1 || block < 64 || block > 1024 || block % 64 != 0) return LBQ_ERR_SHAPE;
+  if (bytes > 0 && !aligned16(buf)) return LBQ_ERR_ALIGN;
+  return hip_status(launch_stream_read(buf, bytes, grid, block, sink, static_cast<hipStream_t>(stream),
+                                       static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)));
+}
+
 lbq_status lbq_rotate(const uint16_t *x, int32_t M, int32_t K, const int8_t *signs, uint16_t *out, void *stream) {
   if (M < 0 || K <= 0 || K % 128 != 0) return LBQ_ERR_SHAPE;
   if (M == 0) return LBQ_OK;

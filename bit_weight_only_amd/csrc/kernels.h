@@ -69,6 +69,12 @@ hipError_t launch_gemm_rtn(const GemmPlan &p, int bits, const void *planes, cons
 hipError_t launch_gemm_pvq(const GemmPlan &p, const void *idx, const void *row_scale, const uint8_t *codebook,
                            const uint16_t *xf, uint16_t *y, int M, int K, int N, void *scratch, hipStream_t s);
 
+// Measurement reference: read bytes (a multiple of 16) at buf once in one
+// launch of grid x block threads; non-null events take the kernel's own
+// begin / end times.
+hipError_t launch_stream_read(const void *buf, size_t bytes, int grid, int block, uint32_t *sink, hipStream_t s,
+                              hipEvent_t start, hipEvent_t stop);
+
 hipError_t launch_unpack_rtn(const void *planes, int K, int N, int bits, uint8_t *codes, hipStream_t s);
 
 // MoE pieces.

@@ -29,7 +29,7 @@ STATUS = {
 EXPORTS = [
     "lbq_status_string", "lbq_packed_bytes", "lbq_pack", "lbq_linear_workspace", "lbq_linear_forward",
     "lbq_linear_forward_path", "lbq_linear_forward_timed", "lbq_moe_workspace", "lbq_moe_forward", "lbq_moe_route", "lbq_unpack_codes",
-    "lbq_rotate", "lbq_linear_forward_noalloc",
+    "lbq_rotate", "lbq_linear_forward_noalloc", "lbq_stream_read",
 ]
 
 
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.lbq_unpack_codes.argtypes = [ctypes.POINTER(Weight), c_vp, c_vp]
         L.lbq_rotate.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]
         L.lbq_linear_forward_noalloc.argtypes = [ctypes.POINTER(Weight), c_vp, c_i32, c_vp, c_vp]
+        L.lbq_stream_read.argtypes = [c_vp, c_sz, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
         for name in EXPORTS:
             if name != "lbq_status_string":
                 getattr(L, name).restype = c_i32

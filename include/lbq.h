@@ -269,6 +269,18 @@ lbq_status lbq_unpack_codes(const lbq_weight *w, uint8_t *codes, void *stream);
 lbq_status lbq_rotate(const uint16_t *x, int32_t M, int32_t K, const int8_t *signs,
                       uint16_t *out, void *stream);
 
+/* Measurement reference, not part of the layer: one launch of grid x block
+ * threads (block a multiple of 64, at most 1024) that reads bytes (a multiple
+ * of 16, below 64 GiB) at buf (device, 16-byte aligned) once, as a plain
+ * streaming read. Its duration for a GEMV launch's byte count is the floor
+ * that launch faces before any decode work, the figure a decode kernel that
+ * tracks bytes moved (Laguna-S-2.1 card, "Reading it honestly") is compared
+ * with beside the HBM peak. sink: device u32 it may write. Optional events as
+ * in lbq_linear_forward_timed (the kernel's own begin and end). bytes = 0 is
+ * an empty launch (the launch floor). */
+lbq_status lbq_stream_read(const void *buf, size_t bytes, int32_t grid, int32_t block, uint32_t *sink,
+                           void *stream, void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif
