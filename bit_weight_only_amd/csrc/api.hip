@@ -166,6 +166,26 @@ lbq_status lbq_pack(const float *W, int32_t K, int32_t N, int32_t bits, int32_t 
   return pack_pvq(W, K, N, signs, codebook, static_cast<uint8_t *>(planes_out), static_cast<uint16_t *>(meta_out));
 }
 
+lbq_status lbq_gptq_factor(const double *H, int32_t K, const int8_t *signs, double damp, double *U) {
+  if (!H || !signs || !U) return LBQ_ERR_NULL;
+  if (K <= 0 || K % 128 != 0) return LBQ_ERR_SHAPE;
+  if (!(damp > 0.0)) return LBQ_ERR_RANGE;
+  for (int k = 0; k < K; ++k)
+    if (signs[k] != 1 && signs[k] != -1) return LBQ_ERR_RANGE;
+  return gptq_factor(H, K, signs, damp, U);
+}
+
+lbq_status lbq_pack_gptq(const float *W, int32_t K, int32_t N, int32_t bits, const int8_t *signs, const double *U,
+                         void *planes_out, void *meta_out) {
+  if (!W || !signs || !U || !planes_out || !meta_out) return LBQ_ERR_NULL;
+  size_t pb, mb;
+  lbq_status st = lbq_packed_bytes(K, N, bits, LBQ_FMT_RTN_PLANES, &pb, &mb);
+  if (st != LBQ_OK) return st;
+  for (int k = 0; k < K; ++k)
+    if (signs[k] != 1 && signs[k] != -1) return LBQ_ERR_RANGE;
+  return pack_gptq(W, K, N, bits, signs, U, static_cast<uint32_t *>(planes_out), static_cast<uint16_t *>(meta_out));
+}
+
 lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes) {
   if (!bytes) return LBQ_ERR_NULL;
   lbq_status st = check_weight(w);

@@ -28,6 +28,10 @@ constexpr int kGroup = 128;
 
 inline double rotation_scale() { return std::sqrt(2.0) / 16.0; }
 
+}  // namespace
+
+namespace lbq {
+
 // Rotate one row of K values in place, per 128-block.
 void rotate_row(double *v, const int8_t *signs, int K) {
   const double c = rotation_scale();
@@ -46,6 +50,12 @@ void rotate_row(double *v, const int8_t *signs, int K) {
     for (int i = 0; i < kGroup; ++i) u[i] *= c;
   }
 }
+
+}  // namespace lbq
+
+namespace {
+
+using lbq::rotate_row;
 
 // Run fn(row_begin, row_end) over [0, N) on all hardware threads.
 template <class F>
@@ -126,6 +136,34 @@ double e4m3_to_f64(uint8_t b) {
   return sign ? -v : v;
 }
 
+void store_group(const uint8_t q[128], int bits, uint16_t s16, uint16_t z16, uint32_t *planes, uint16_t *meta) {
+  for (int p = 0; p < bits; ++p) {
+    for (int w4 = 0; w4 < 4; ++w4) {
+      uint32_t word = 0;
+      for (int j = 0; j < 32; ++j) word |= static_cast<uint32_t>((q[32 * w4 + j] >> p) & 1u) << j;
+      planes[p * 4 + w4] = word;
+    }
+  }
+  meta[0] = s16;
+  meta[1] = z16;
+}
+
+bool group_scale(const double *u, int stride, int bits, uint16_t &s16, double &s, double &z) {
+  double mn = 0.0, mx = 0.0;
+  for (int i = 0; i < kGroup; ++i) {
+    const double v = u[static_cast<size_t>(i) * stride];
+    if (v < mn) mn = v;
+    if (v > mx) mx = v;
+  }
+  const double L = static_cast<double>((1 << bits) - 1);
+  s16 = f64_to_f16_rne((mx - mn) / L);
+  if ((s16 & 0x7FFFu) >= 0x5800u) return false;   // s >= 128 (or not finite)
+  if (s16 == 0) s16 = 0x3C00u;                     // degenerate group: scale 1
+  s = f16_to_f64(s16);
+  z = std::rint(-mn / s) + 0.0;
+  return true;
+}
+
 lbq_status pack_rtn(const float *W, int K, int N, int bits, const int8_t *signs, uint32_t *planes,
                     uint16_t *meta) {
   const int G = K / kGroup;
@@ -145,37 +183,21 @@ lbq_status pack_rtn(const float *W, int K, int N, int bits, const int8_t *signs,
       rotate_row(v.data(), signs, K);
       for (int g = 0; g < G; ++g) {
         const double *u = v.data() + g * kGroup;
-        double mn = 0.0, mx = 0.0;
-        for (int i = 0; i < kGroup; ++i) {
-          if (u[i] < mn) mn = u[i];
-          if (u[i] > mx) mx = u[i];
-        }
-        uint16_t s16 = f64_to_f16_rne((mx - mn) / L);
+        uint16_t s16;
+        double s, z;
         // the GEMM's decode needs finite -64 s and -16 s z in fp16: s < 128
-        if ((s16 & 0x7FFFu) >= 0x5800u) {
+        if (!group_scale(u, 1, bits, s16, s, z)) {
           err = LBQ_ERR_RANGE;
           return;
         }
-        if (s16 == 0) s16 = 0x3C00u;  // degenerate group: scale 1
-        const double s = f16_to_f64(s16);
-        const double z = std::rint(-mn / s) + 0.0;
         uint8_t q[kGroup];
         for (int i = 0; i < kGroup; ++i) {
           double c = std::rint(u[i] / s) + z;
           c = std::min(std::max(c, 0.0), L);
           q[i] = static_cast<uint8_t>(c);
         }
-        uint32_t *pl = planes + (static_cast<size_t>(n) * G + g) * bits * 4;
-        for (int p = 0; p < bits; ++p) {
-          for (int w4 = 0; w4 < 4; ++w4) {
-            uint32_t word = 0;
-            for (int j = 0; j < 32; ++j) word |= static_cast<uint32_t>((q[32 * w4 + j] >> p) & 1u) << j;
-            pl[p * 4 + w4] = word;
-          }
-        }
-        uint16_t *mt = meta + (static_cast<size_t>(n) * G + g) * 2;
-        mt[0] = s16;
-        mt[1] = f64_to_f16_rne(z);
+        store_group(q, bits, s16, f64_to_f16_rne(z), planes + (static_cast<size_t>(n) * G + g) * bits * 4,
+                    meta + (static_cast<size_t>(n) * G + g) * 2);
       }
     }
   });

@@ -10,6 +10,16 @@ uint16_t f64_to_f16_rne(double x);
 double f16_to_f64(uint16_t h);
 double e4m3_to_f64(uint8_t b);
 
+// Rotation of one row of K values in place, per 128-block (signs, radix-2
+// butterflies, sqrt(2)/16), float64.
+void rotate_row(double *v, const int8_t *signs, int K);
+// Scale and zero of one 128-group whose values sit at u[i * stride]: the
+// zero-inclusive range rule, s as fp16 (degenerate 0 -> 1), z = rint(-mn / s).
+// false when s >= 128 (the RTN GEMM's fp16 decode constants).
+bool group_scale(const double *u, int stride, int bits, uint16_t &s16, double &s, double &z);
+// Bit-planes of one group's 128 codes and its (s, z) fp16 pair.
+void store_group(const uint8_t q[128], int bits, uint16_t s16, uint16_t z16, uint32_t *planes, uint16_t *meta);
+
 // RTN bit-plane packing of W [N][K] (fp32, host) into planes [N][K/128][bits][4]
 // and meta [N][K/128][2] fp16 bit patterns (scale, zero).
 lbq_status pack_rtn(const float *W, int K, int N, int bits, const int8_t *signs, uint32_t *planes,
@@ -18,5 +28,12 @@ lbq_status pack_rtn(const float *W, int K, int N, int bits, const int8_t *signs,
 // Product-VQ packing of W [N][K] into idx [N][K/4] and fp16 row scales [N].
 lbq_status pack_pvq(const float *W, int K, int N, const int8_t *signs, const uint8_t *codebook,
                     uint8_t *idx, uint16_t *scale);
+
+// GPTQ: the upper Cholesky factor U of (R H R^T + damp mean(diag) I)^-1 of a
+// host Hessian H [K][K] (original basis), and packing with error feedback
+// through U (gptq.cpp).
+lbq_status gptq_factor(const double *H, int K, const int8_t *signs, double damp, double *U);
+lbq_status pack_gptq(const float *W, int K, int N, int bits, const int8_t *signs, const double *U,
+                     uint32_t *planes, uint16_t *meta);
 
 }  // namespace lbq

@@ -29,7 +29,8 @@ STATUS = {
 EXPORTS = [
     "lbq_status_string", "lbq_packed_bytes", "lbq_pack", "lbq_linear_workspace", "lbq_linear_forward",
     "lbq_linear_forward_path", "lbq_linear_forward_timed", "lbq_moe_workspace", "lbq_moe_forward", "lbq_moe_route", "lbq_unpack_codes",
-    "lbq_rotate", "lbq_linear_forward_noalloc", "lbq_stream_read",
+    "lbq_rotate", "lbq_linear_forward_noalloc", "lbq_stream_read", "lbq_gptq_factor",
+    "lbq_pack_gptq",
 ]
 
 
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.lbq_rotate.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]
         L.lbq_linear_forward_noalloc.argtypes = [ctypes.POINTER(Weight), c_vp, c_i32, c_vp, c_vp]
         L.lbq_stream_read.argtypes = [c_vp, c_sz, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
+        L.lbq_gptq_factor.argtypes = [c_vp, c_i32, c_vp, ctypes.c_double, c_vp]
+        L.lbq_pack_gptq.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
         for name in EXPORTS:
             if name != "lbq_status_string":
                 getattr(L, name).restype = c_i32
@@ -130,6 +133,30 @@ def pack(W: np.ndarray, bits: int, signs: np.ndarray, fmt: int = FMT_RTN_PLANES,
     st = lib().lbq_pack(W.ctypes.data, K, N, bits, fmt, signs.ctypes.data,
                         None if cb is None else cb.ctypes.data, planes.ctypes.data, meta.ctypes.data)
     _check(st, "lbq_pack")
+    return planes, meta
+
+
+def gptq_factor(H: np.ndarray, signs: np.ndarray, damp: float = 0.01) -> np.ndarray:
+    """lbq_gptq_factor: U [K][K] float64 from a host Hessian H [K][K] (original basis)."""
+    H = np.ascontiguousarray(H, dtype=np.float64)
+    K = H.shape[0]
+    signs = np.ascontiguousarray(signs, dtype=np.int8)
+    U = np.empty((K, K), dtype=np.float64)
+    _check(lib().lbq_gptq_factor(H.ctypes.data, K, signs.ctypes.data, float(damp), U.ctypes.data), "lbq_gptq_factor")
+    return U
+
+
+def pack_gptq(W: np.ndarray, bits: int, signs: np.ndarray, U: np.ndarray):
+    """lbq_pack_gptq: (planes, meta) uint8 arrays in the RTN bit-plane format."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    signs = np.ascontiguousarray(signs, dtype=np.int8)
+    U = np.ascontiguousarray(U, dtype=np.float64)
+    pb, mb = packed_bytes(K, N, bits, FMT_RTN_PLANES)
+    planes = np.empty(pb, dtype=np.uint8)
+    meta = np.empty(mb, dtype=np.uint8)
+    _check(lib().lbq_pack_gptq(W.ctypes.data, K, N, bits, signs.ctypes.data, U.ctypes.data, planes.ctypes.data,
+                               meta.ctypes.data), "lbq_pack_gptq")
     return planes, meta
 
 

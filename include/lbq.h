@@ -158,6 +158,35 @@ lbq_status lbq_pack(const float *W, int32_t K, int32_t N, int32_t bits, int32_t 
                     const int8_t *signs, const uint8_t *codebook,
                     void *planes_out, void *meta_out);
 
+/* GPTQ, step 1 (host, offline): the factor the error feedback of
+ * lbq_pack_gptq runs through. The weights are quantized with group-128 GPTQ in
+ * the Hadamard-rotated basis (LLaDA2.2-mini card, property table, "Routed
+ * Experts" row; Qwen3.8-27B Pingala-8 card, "What this is": LDLQ rounding
+ * behind a random Hadamard rotation).
+ *   H: host float64 [K][K], symmetric positive semi-definite proxy Hessian of
+ *      the layer input in the original basis (e.g. X^T X / n of calibration
+ *      activations X [n][K]).
+ *   signs: host int8 [K] of +-1 (the weight's rotation signs).
+ *   damp: > 0; damp * mean(diag H') is added to the diagonal of H'.
+ *   U: host float64 [K][K] out: the upper Cholesky factor of H'^-1
+ *      (H'^-1 = U^T U), H' = R H R^T + damping; zeros below the diagonal.
+ * O(K^3) on the host threads. Errors: LBQ_ERR_NULL, LBQ_ERR_SHAPE (K not a
+ * positive multiple of 128), LBQ_ERR_RANGE (signs not +-1, non-finite H, a
+ * zero diagonal mean, or H' not positive definite after damping). */
+lbq_status lbq_gptq_factor(const double *H, int32_t K, const int8_t *signs, double damp, double *U);
+
+/* GPTQ, step 2 (host, offline): pack W [N][K] (host fp32, as lbq_pack) into
+ * the RTN bit-plane format (same planes / meta layout and sizes), choosing the
+ * codes with error feedback through U (from lbq_gptq_factor): rotate each row;
+ * then for each column j in order, at the first column of each 128-group the
+ * group's scale and zero from its current values (the lbq_pack RTN rule),
+ * q = clamp(rint(w_j / s) + z, 0, 2^b - 1), e = (w_j - (q - z) s) / U[j][j],
+ * and w_k -= e U[j][k] for every later column k. Float64; the result depends
+ * only on (W, signs, U, bits). Errors as lbq_pack (RTN), plus LBQ_ERR_RANGE
+ * for a non-positive diagonal of U. */
+lbq_status lbq_pack_gptq(const float *W, int32_t K, int32_t N, int32_t bits, const int8_t *signs,
+                         const double *U, void *planes_out, void *meta_out);
+
 /* Workspace bytes lbq_linear_forward needs for M tokens (host query; the
  * rotated activations, the GEMM's zero-point sums and its split-K partial
  * tiles and counters). Errors as lbq_linear_forward's argument checks. */

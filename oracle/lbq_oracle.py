@@ -157,6 +157,21 @@ def rtn_quantize(wrot: np.ndarray, bits: int):
     return q.reshape(n, k).astype(np.uint8), s16, z16
 
 
+def group_params(wg: np.ndarray, bits: int):
+    """fp16 scale and zero of one column block of groups, the rule rtn_quantize
+    uses: mn = min(0, min w'), mx = max(0, max w'), s = fp16((mx - mn) / L)
+    (0 -> 1), z = rint(-mn / s). wg: [N][128] float64. Returns (s16, z16)."""
+    lvl = float(2 ** bits - 1)
+    mn = np.minimum(wg.min(axis=-1), 0.0)
+    mx = np.maximum(wg.max(axis=-1), 0.0)
+    s16 = to_fp16((mx - mn) / lvl)
+    if not np.all(np.isfinite(s16)):
+        raise RangeError("scale overflows fp16")
+    s16 = np.where(s16 == 0, np.float16(1.0), s16)
+    z = np.rint(-mn / s16.astype(np.float64)) + 0.0
+    return s16, to_fp16(z)
+
+
 def dequantize(q: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
     """W'_hat[n, k] = (q[n, k] - z[n, g]) * s[n, g] in float64, g = k // 128."""
     n, k = q.shape
@@ -164,6 +179,84 @@ def dequantize(q: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
     z = z16.astype(np.float64)[..., None]
     s = s16.astype(np.float64)[..., None]
     return ((qg - z) * s).reshape(n, k)
+
+
+# ---------------------------------------------------------------------------
+# GPTQ in the rotated basis (LLaDA2.2-mini card, property table, "Routed
+# Experts" row: group-128 GPTQ in a Hadamard-rotated basis; Qwen3.8-27B
+# Pingala-8 card, "What this is": LDLQ rounding behind a random Hadamard
+# rotation, the same error feedback). Codes go column by column; each
+# column's rounding error, scaled by the inverse Hessian's Cholesky factor, is
+# pushed onto the columns not yet quantized. The stored format is the RTN one.
+#
+# Readings (the pages name the method, not its settings): H is the caller's
+# proxy Hessian of the layer input (e.g. X^T X of calibration activations) in
+# the original basis; in the rotated basis it is H' = R H R^T. Dampening adds
+# 0.01 * mean(diag H') to the diagonal. Columns go in natural order (no
+# reordering, so 128-groups stay the rotation blocks). A group's scale and zero
+# come from its columns as they stand when its first column is reached (after
+# the feedback from earlier groups), by the RTN rule. The feedback is applied
+# one column at a time (the unblocked form of the algorithm).
+# ---------------------------------------------------------------------------
+
+def gptq_hessian_rotated(h: np.ndarray, signs: np.ndarray, damp: float = 0.01) -> np.ndarray:
+    """H' = R H R^T plus damp * mean(diag H') on the diagonal (float64 [K][K])."""
+    h = np.asarray(h, dtype=np.float64)
+    a = rotate(h, signs)              # row i: R h_i, i.e. H R^T
+    hr = rotate(a.T, signs).T         # R (H R^T)
+    d = damp * float(np.mean(np.diag(hr)))
+    if not d > 0.0:
+        raise RangeError("Hessian has no positive diagonal")
+    hr = hr + d * np.eye(hr.shape[0])
+    return hr
+
+
+def gptq_factor(h: np.ndarray, signs: np.ndarray, damp: float = 0.01) -> np.ndarray:
+    """U: the upper Cholesky factor of H'^-1 (H'^-1 = U^T U), float64 [K][K]."""
+    hinv = np.linalg.inv(gptq_hessian_rotated(h, signs, damp))
+    hinv = (hinv + hinv.T) / 2.0
+    return np.linalg.cholesky(hinv).T
+
+
+def gptq_quantize(wrot: np.ndarray, u: np.ndarray, bits: int):
+    """Codes, fp16 scale and zero of a rotated weight [N][K] by GPTQ with the
+    factor u. For column j (group g = j // 128): at the group's first column
+    its (s, z) come from the current columns; q = clamp(rint(w_j / s) + z, 0, L);
+    e = (w_j - (q - z) s) / u[j, j]; then w_k -= e * u[j, k] for every k > j.
+    Returns q (uint8 [N][K]), s16, z16 (float16 [N][K/128])."""
+    if bits not in (2, 3, 4):
+        raise ValueError("bits must be 2, 3 or 4")
+    w = np.array(wrot, dtype=np.float64)
+    if not np.all(np.isfinite(w)):
+        raise RangeError("non-finite weight")
+    n, k = w.shape
+    lvl = float(2 ** bits - 1)
+    q = np.zeros((n, k), dtype=np.uint8)
+    s16 = np.zeros((n, k // GROUP), dtype=np.float16)
+    z16 = np.zeros((n, k // GROUP), dtype=np.float16)
+    s = z = None
+    for j in range(k):
+        g = j // GROUP
+        if j % GROUP == 0:
+            s16[:, g], z16[:, g] = group_params(w[:, j:j + GROUP], bits)
+            s = s16[:, g].astype(np.float64)
+            z = z16[:, g].astype(np.float64)
+        qj = np.clip(np.rint(w[:, j] / s) + z, 0.0, lvl)
+        err = (w[:, j] - (qj - z) * s) / u[j, j]
+        w[:, j + 1:] -= np.outer(err, u[j, j + 1:])
+        q[:, j] = qj.astype(np.uint8)
+    return q, s16, z16
+
+
+def pack_gptq(w: np.ndarray, bits: int, signs: np.ndarray, u: np.ndarray):
+    """Offline GPTQ packing of one fp32 weight [N][K] with the factor u of
+    gptq_factor: rotate, quantize with error feedback, bit-planes. Returns
+    (planes, meta, codes) as pack_rtn."""
+    w = np.asarray(w)
+    if not np.all(np.isfinite(w)):
+        raise RangeError("non-finite weight")
+    q, s16, z16 = gptq_quantize(rotate(w.astype(np.float64), signs), u, bits)
+    return pack_planes(q, bits), pack_meta(s16, z16), q
 
 
 # ---------------------------------------------------------------------------
@@ -369,7 +462,6 @@ def moe_forward(x16: np.ndarray, logits: np.ndarray, top_k: int, expert_weights=
             o = expert_ffn(np.asarray(x16)[rows], w_gu, w_dn)
         y[rows] += wts[rows, slots][:, None] * o
     return y
-
 
 
 def moe_forward_per_assignment(x16, logits, top_k, expert_weights) -> np.ndarray:

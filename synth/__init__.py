@@ -75,6 +75,28 @@ def codebook(workload: int = 0, item: int = 0, entries: int = 256, dim: int = 4)
         it += 1000
 
 
+ROLE_CALIB = 6
+
+
+def calibration(n: int, k: int, workload: int = 0, item: int = 0, sample: int = 0,
+                rank_frac: float = 0.25) -> np.ndarray:
+    """fp32 [n][k] stand-in for activations of a layer input: a low-rank
+    correlated part (rank k * rank_frac) plus 0.1 isotropic noise, each channel
+    scaled by a log-normal factor (a few channels much larger than the rest, as
+    in transformer activations). The structure (mixing matrix, channel scales)
+    is fixed by (workload, item); `sample` draws other rows of the same
+    distribution (calibration rows, then held-out rows)."""
+    g = rng(workload, item, ROLE_CALIB)
+    r = max(1, int(k * rank_frac))
+    mix = g.standard_normal((r, k), dtype=np.float32) * np.float32(1.0 / np.sqrt(r))
+    scale = np.exp(np.float32(0.5) * g.standard_normal(k, dtype=np.float32))
+    gs = np.random.default_rng([2026, int(workload), int(item), ROLE_CALIB, int(sample)])
+    x = gs.standard_normal((n, r), dtype=np.float32) @ mix
+    x += np.float32(0.1) * gs.standard_normal((n, k), dtype=np.float32)
+    x *= scale[None, :]
+    return x
+
+
 # Workload shapes. (K, N) is (inputs, outputs) of a linear.
 SINGLE_LINEAR = dict(K=4096, N=4096, M=1, bits=2)
 DENSE_STACK_SHAPES = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672), ("down", 14336, 4096)]

@@ -261,3 +261,81 @@ def test_host_pack_matches_hand_derived_groups(L, golden_dir):
         assert np.array_equal(planes.view(np.uint32).reshape(c["bits"], 4), np.array(c["planes"], np.uint32)), c["name"]
         sz = meta.view(np.uint16)
         assert int(sz[0]) == c["scale_bits"] and int(sz[1]) == c["zero_bits"], c["name"]
+
+
+# ---------------------------------------------------------------- GPTQ (host packer)
+
+def _gptq_inputs(k, n, item):
+    x = synth.calibration(2 * k, k, workload=41, item=item).astype(np.float64)
+    h = x.T @ x / x.shape[0]
+    return h, synth.signs(k, workload=41, item=item), synth.weights(n, k, workload=41, item=item)
+
+
+@pytest.mark.parametrize("k", [256, 1024])
+def test_gptq_factor_matches_oracle(L, k):
+    """The library's factor (Cholesky taken from the last column back, then a
+    triangular inverse) against the oracle's (inverse, then Cholesky):
+    the same matrix up to floating-point rounding."""
+    h, s, _ = _gptq_inputs(k, 8, k)
+    u = L.gptq_factor(h, s)
+    uo = O.gptq_factor(h, s)
+    assert np.max(np.abs(u - uo)) <= 1e-11 * np.max(np.abs(uo))
+    assert np.all(np.tril(u, -1) == 0.0)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_gptq_pack_byte_identical_given_the_same_factor(L, bits):
+    """Given the same factor the host packer and the oracle take the same steps
+    in the same order: identical planes and scale/zero words."""
+    k, n = 1024, 200
+    h, s, w = _gptq_inputs(k, n, 7)
+    uo = O.gptq_factor(h, s)
+    planes, meta = L.pack_gptq(w, bits, s, uo)
+    op, om, q = O.pack_gptq(w, bits, s, uo)
+    assert np.array_equal(planes, op.view(np.uint8).reshape(-1))
+    assert np.array_equal(meta, om.view(np.uint8).reshape(-1))
+    # with the library's own factor the codes come out the same too (no
+    # rounding decision in this seeded case is within the factors' difference)
+    pl2, _ = L.pack_gptq(w, bits, s, L.gptq_factor(h, s))
+    assert np.array_equal(O.unpack_planes(pl2.view(np.uint32), bits, k), q)
+
+
+def test_gptq_full_single_linear_sampled_rows(L):
+    """4096 x 4096 at 2 bits: the library packs every row; the oracle packs 24
+    sampled rows with the same factor (rows are independent given it)."""
+    k = n = 4096
+    h, s, _ = _gptq_inputs(k, 1, 11)
+    w = synth.weights(n, k, workload=synth.W_SINGLE)
+    uo = O.gptq_factor(h, s)
+    planes, meta = L.pack_gptq(w, 2, s, uo)
+    rows = np.sort(np.random.default_rng(2).choice(n, 24, replace=False))
+    op, om, _ = O.pack_gptq(w[rows], 2, s, uo)
+    rb, mb = k * 2 // 8, (k // 128) * 4
+    for i, r in enumerate(rows):
+        assert np.array_equal(planes[r * rb:(r + 1) * rb], op[i].view(np.uint8).reshape(-1)), r
+        assert np.array_equal(meta[r * mb:(r + 1) * mb], om[i].view(np.uint8).reshape(-1)), r
+
+
+def test_gptq_errors(L):
+    k = 256
+    h, s, w = _gptq_inputs(k, 4, 3)
+    with pytest.raises(L.LbqError) as e:
+        L.gptq_factor(np.zeros((k, k)), s)
+    assert e.value.status == -6
+    with pytest.raises(L.LbqError) as e:
+        L.gptq_factor(h[:200, :200], s[:200])
+    assert e.value.status == -2
+    bad = s.copy()
+    bad[3] = 0
+    with pytest.raises(L.LbqError) as e:
+        L.gptq_factor(h, bad)
+    assert e.value.status == -6
+    u = L.gptq_factor(h, s)
+    with pytest.raises(L.LbqError) as e:
+        L.pack_gptq(w, 5, s, u)
+    assert e.value.status == -3
+    u_bad = u.copy()
+    u_bad[7, 7] = 0.0
+    with pytest.raises(L.LbqError) as e:
+        L.pack_gptq(w, 2, s, u_bad)
+    assert e.value.status == -6

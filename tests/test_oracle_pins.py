@@ -456,3 +456,106 @@ def test_rel_l2_hand_values():
     assert O.rel_l2(np.zeros(3), np.zeros(3)) == 0.0
     # fp16 inputs are widened exactly before the norms
     assert O.rel_l2(np.array([1.0, 2.0], np.float16), np.array([1.0, 1.0], np.float16)) == 1.0 / np.sqrt(2.0)
+
+
+# ---------------------------------------------------------------- GPTQ
+
+def _dense_rotation(signs):
+    """R = blockdiag(c H_128 diag(s)) built from scipy's Hadamard matrix."""
+    k = len(signs)
+    h = scipy.linalg.hadamard(128).astype(np.float64) / math.sqrt(128.0)
+    r = np.zeros((k, k))
+    for b in range(k // 128):
+        sl = slice(128 * b, 128 * b + 128)
+        r[sl, sl] = h * np.asarray(signs[sl], np.float64)[None, :]
+    return r
+
+
+def _hessian(n_samples, k, item):
+    x = synth.calibration(n_samples, k, workload=40, item=item).astype(np.float64)
+    return x.T @ x / n_samples
+
+
+def test_gptq_rotated_hessian_is_r_h_rt_plus_damping():
+    k = 256
+    s = synth.signs(k, workload=40, item=1)
+    h = _hessian(512, k, 1)
+    r = _dense_rotation(s)
+    want = r @ h @ r.T
+    want += 0.01 * np.mean(np.diag(want)) * np.eye(k)
+    got = O.gptq_hessian_rotated(h, s)
+    assert np.max(np.abs(got - want)) < 1e-12 * np.max(np.abs(want))
+    u = O.gptq_factor(h, s)
+    assert np.allclose(np.triu(u), u)                            # upper triangular
+    assert np.allclose(u.T @ u @ got, np.eye(k), atol=1e-8)      # U^T U = H'^-1
+
+
+def test_gptq_without_feedback_is_rtn():
+    """A Hessian that is diagonal in the rotated basis (H = R^T D R) leaves no
+    error to feed forward: the codes, scales and zeros are RTN's."""
+    k, n = 256, 16
+    s = synth.signs(k, workload=40, item=2)
+    r = _dense_rotation(s)
+    d = np.exp(np.random.default_rng(3).standard_normal(k))
+    h = r.T @ np.diag(d) @ r
+    u = O.gptq_factor(h, s)
+    w = synth.weights(n, k, workload=40, item=2)
+    wrot = O.rotate(w.astype(np.float64), s)
+    for bits in (2, 3, 4):
+        q, s16, z16 = O.gptq_quantize(wrot, u, bits)
+        q0, s0, z0 = O.rtn_quantize(wrot, bits)
+        assert np.array_equal(q, q0) and np.array_equal(s16, s0) and np.array_equal(z16, z0), bits
+
+
+def test_gptq_matches_textbook_obs_updates():
+    """The Cholesky form against the optimal-brain-surgeon sequence it is
+    derived from: keep the full inverse Hessian of the columns not yet
+    quantized; after column j, w_rest -= e_j Hinv[j, rest] with
+    e_j = (w_j - q_j) / Hinv[j, j], and Hinv loses row and column j by the
+    Schur complement. Same codes (no rounding tie is near in this seeded case)."""
+    k, n = 256, 12
+    s = synth.signs(k, workload=40, item=4)
+    h = _hessian(600, k, 4)
+    hr = O.gptq_hessian_rotated(h, s)
+    w = synth.weights(n, k, workload=40, item=4)
+    wrot = O.rotate(w.astype(np.float64), s)
+    for bits in (2, 4):
+        q, s16, z16 = O.gptq_quantize(wrot, O.gptq_factor(h, s), bits)
+        lvl = 2 ** bits - 1
+        ww = wrot.copy()
+        hinv = np.linalg.inv(hr)
+        q_ref = np.zeros((n, k), np.uint8)
+        for j in range(k):
+            if j % 128 == 0:   # group range from the current columns, zero included
+                grp = ww[:, j:j + 128]
+                mn, mx = np.minimum(grp.min(1), 0), np.maximum(grp.max(1), 0)
+                sc = ((mx - mn) / lvl).astype(np.float16).astype(np.float64)
+                sc[sc == 0] = 1.0
+                zz = np.rint(-mn / sc)
+            qj = np.clip(np.rint(ww[:, j] / sc) + zz, 0, lvl)
+            e = (ww[:, j] - (qj - zz) * sc) / hinv[j, j]
+            ww[:, j + 1:] -= np.outer(e, hinv[j, j + 1:])
+            hinv = hinv - np.outer(hinv[:, j], hinv[j, :]) / hinv[j, j]
+            q_ref[:, j] = qj
+        assert np.array_equal(q, q_ref), (bits, int((q != q_ref).sum()))
+
+
+def test_gptq_lowers_the_layer_output_error():
+    """GPTQ's purpose: a smaller proxy loss tr(E H' E^T), E the rotated-basis
+    weight error, than RTN on correlated calibration data (the property that
+    makes it worth its cost; not a pinned value)."""
+    k, n = 512, 64
+    s = synth.signs(k, workload=40, item=5)
+    h = _hessian(1024, k, 5)
+    hr = O.gptq_hessian_rotated(h, s, damp=0.0 + 1e-12)
+    u = O.gptq_factor(h, s)
+    w = synth.weights(n, k, workload=40, item=5)
+    wrot = O.rotate(w.astype(np.float64), s)
+    for bits in (2, 3):
+        q, s16, z16 = O.gptq_quantize(wrot, u, bits)
+        q0, s0, z0 = O.rtn_quantize(wrot, bits)
+        e_g = O.dequantize(q, s16, z16) - wrot
+        e_r = O.dequantize(q0, s0, z0) - wrot
+        loss_g = np.trace(e_g @ hr @ e_g.T)
+        loss_r = np.trace(e_r @ hr @ e_r.T)
+        assert loss_g < 0.8 * loss_r, (bits, loss_g / loss_r)
