@@ -121,9 +121,13 @@ def e4m3_to_float(b) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # Group-128 asymmetric round-to-nearest codes (LLaDA2.2-mini card: group-128
-# GPTQ codes at 2/3/4 bits in the rotated basis; RTN is the plain quantizer
-# GPTQ's own rounding grid is defined by)
+# GPTQ codes at 2/3/4 bits in the rotated basis for the routed experts, 8-bit
+# codes for the non-expert path and the readout (property table, "Non-Expert
+# Path" and "Readout & Embeddings" rows); RTN is the plain quantizer GPTQ's own
+# rounding grid is defined by)
 # ---------------------------------------------------------------------------
+
+CODE_BITS = (2, 3, 4, 8)
 
 def rtn_quantize(wrot: np.ndarray, bits: int):
     """Codes, fp16 scale and fp16 zero per (row, 128-group) of a rotated weight.
@@ -135,8 +139,8 @@ def rtn_quantize(wrot: np.ndarray, bits: int):
     fp16-rounded s is the one used for the codes.
     Returns q (uint8 [N][K]), s16 and z16 (float16 [N][K/128]).
     """
-    if bits not in (2, 3, 4):
-        raise ValueError("bits must be 2, 3 or 4")
+    if bits not in CODE_BITS:
+        raise ValueError("bits must be 2, 3, 4 or 8")
     wrot = np.asarray(wrot, dtype=np.float64)
     if not np.all(np.isfinite(wrot)):
         raise RangeError("non-finite weight")
@@ -224,8 +228,8 @@ def gptq_quantize(wrot: np.ndarray, u: np.ndarray, bits: int):
     its (s, z) come from the current columns; q = clamp(rint(w_j / s) + z, 0, L);
     e = (w_j - (q - z) s) / u[j, j]; then w_k -= e * u[j, k] for every k > j.
     Returns q (uint8 [N][K]), s16, z16 (float16 [N][K/128])."""
-    if bits not in (2, 3, 4):
-        raise ValueError("bits must be 2, 3 or 4")
+    if bits not in CODE_BITS:
+        raise ValueError("bits must be 2, 3, 4 or 8")
     w = np.array(wrot, dtype=np.float64)
     if not np.all(np.isfinite(w)):
         raise RangeError("non-finite weight")
@@ -290,6 +294,17 @@ def unpack_planes(planes: np.ndarray, bits: int, k: int) -> np.ndarray:
         bitp = (planes[:, :, p, :, None] >> j) & np.uint32(1)
         q |= bitp << np.uint32(p)
     return q.reshape(n, k).astype(np.uint8)
+
+
+def split_nibbles(planes: np.ndarray) -> tuple:
+    """The 8-bit codes' planes split into a low-nibble and a high-nibble plane
+    set (LLaDA2.2-mini card, file list: the readout's codes also stored as
+    high/low nibble planes). planes: uint32 [N][G][8][4]; returns (lo, hi),
+    each uint32 [N][G][4][4]: planes 0..3 and 4..7, so q = lo + 16 hi."""
+    p = np.asarray(planes).view(np.uint32)
+    n = p.shape[0]
+    p = p.reshape(n, -1, 8, 4)
+    return np.ascontiguousarray(p[:, :, :4, :]), np.ascontiguousarray(p[:, :, 4:, :])
 
 
 def pack_meta(s16: np.ndarray, z16: np.ndarray) -> np.ndarray:

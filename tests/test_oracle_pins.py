@@ -156,7 +156,7 @@ def test_e4m3_golden_and_torch(golden_dir):
 
 # ---------------------------------------------------------------- RTN codes
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_rtn_codes_are_nearest_grid_point(bits):
     lvl = 2 ** bits - 1
     s = synth.signs(256, workload=9, item=3)
@@ -180,7 +180,7 @@ def test_rtn_codes_are_nearest_grid_point(bits):
                 assert q[n, g * 128 + i] in winners
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_codes_are_fixed_point_of_dequantize_then_assign(bits):
     s = synth.signs(512, workload=9, item=4)
     w = synth.weights(16, 512, workload=9, item=10 + bits)
@@ -260,6 +260,25 @@ def test_plane_words_closed_form(bits, words):
     assert np.all(full == 0xFFFFFFFF)
 
 
+def test_plane_words_closed_form_8bit_and_nibble_split():
+    """Codes 0..255 over two groups: word w of group g holds codes 128 g + 32 w
+    + i, so planes 0..4 follow the bit patterns of i, plane 5 is bit 0 of w,
+    plane 6 bit 1 of w, plane 7 the group index (derived by hand). The nibble
+    split keeps planes 0..3 (q mod 16) and 4..7 (q div 16)."""
+    q = np.arange(256, dtype=np.uint8)[None, :]
+    pl = O.pack_planes(q, 8)
+    low = [0xAAAAAAAA, 0xCCCCCCCC, 0xF0F0F0F0, 0xFF00FF00, 0xFFFF0000]
+    for g in range(2):
+        for p in range(5):
+            assert np.all(pl[0, g, p, :] == low[p]), (g, p)
+        assert list(pl[0, g, 5, :]) == [0, 0xFFFFFFFF, 0, 0xFFFFFFFF]
+        assert list(pl[0, g, 6, :]) == [0, 0, 0xFFFFFFFF, 0xFFFFFFFF]
+        assert np.all(pl[0, g, 7, :] == (0xFFFFFFFF if g else 0))
+    lo, hi = O.split_nibbles(pl)
+    assert np.array_equal(O.unpack_planes(lo, 4, 256), q & 15)
+    assert np.array_equal(O.unpack_planes(hi, 4, 256), q >> 4)
+
+
 def test_single_code_lands_in_its_word_and_bit():
     for pos in [0, 31, 32, 77, 127, 128 + 65]:
         q = np.zeros((1, 256), np.uint8)
@@ -272,7 +291,7 @@ def test_single_code_lands_in_its_word_and_bit():
         assert np.array_equal(pl[0], expect)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_unpack_inverts_pack(bits):
     q = np.random.default_rng(5).integers(0, 2 ** bits, size=(3, 384)).astype(np.uint8)
     assert np.array_equal(O.unpack_planes(O.pack_planes(q, bits), bits, 384), q)
@@ -314,6 +333,18 @@ def test_quantized_linear_is_close_to_unquantized_at_4_bits():
 
 
 # ---------------------------------------------------------------- router / MoE
+
+def test_quantized_linear_is_close_to_unquantized_at_8_bits():
+    """8-bit group codes (the non-expert path's width): a step of about 1/255
+    of each group's range leaves a relative output error near 0.006."""
+    k, n = 1024, 64
+    s = synth.signs(k, workload=9, item=8)
+    w = synth.weights(n, k, workload=9, item=8)
+    x = synth.activations(3, k, workload=9, item=8)
+    planes, meta, _ = O.pack_rtn(w, 8, s)
+    y = O.linear_rtn(x, planes, meta, s, 8, n, k)
+    assert O.rel_l2(y, x.astype(np.float64) @ w.astype(np.float64).T) < 0.015
+
 
 def test_route_against_full_sort_and_softmax():
     lg = synth.logits(16, 32, workload=9)
