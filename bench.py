@@ -84,9 +84,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+# sources each profiled kernel is built from (a counter summary is stale once they change)
+KERNEL_SOURCES = {
+    "gemv_mfma_kernel": DOMINANT_SOURCES,
+    "gemm_rtn_kernel": ["bit_weight_only_amd/csrc/gemm_rtn.hip", "bit_weight_only_amd/csrc/gemm_common.h",
+                        "bit_weight_only_amd/csrc/device.h"],
+    "gemm_pvq_kernel": ["bit_weight_only_amd/csrc/gemm.hip", "bit_weight_only_amd/csrc/gemm_common.h",
+                        "bit_weight_only_amd/csrc/device.h"],
+    "moe_mx_kernel": ["bit_weight_only_amd/csrc/moe_mx.hip", "bit_weight_only_amd/csrc/mx_core.h",
+                      "bit_weight_only_amd/csrc/gemm_common.h", "bit_weight_only_amd/csrc/device.h"],
+}
+
+
+def source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in DOMINANT_SOURCES:
+    for p in (sources or DOMINANT_SOURCES):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -603,9 +615,10 @@ def extra_pvq(torch, L, steps, Ms=None):
     return res
 
 
-def extra_moe(torch, L, steps, extras=True):
+def extra_moe(torch, L, steps, extras=True, M=None):
     cfg = synth.MOE_BLOCK
-    E, H, F, k, M = cfg["E"], cfg["hidden"], cfg["ffn"], cfg["top_k"], cfg["M"]
+    E, H, F, k = cfg["E"], cfg["hidden"], cfg["ffn"], cfg["top_k"]
+    M = M or cfg["M"]
     dev = torch.device("cuda:0")
     bits = synth.expert_bits(E, workload=synth.W_MOE)
     sh = synth.signs(H, workload=synth.W_MOE, item=1)
@@ -645,7 +658,8 @@ def extra_moe(torch, L, steps, extras=True):
     nbytes = float(np.mean(touched))
     flops = 2.0 * M * k * (2 * F * H + H * F)
     out = {"M": M, "us_per_block": round(per * 1e6, 2), "touched_bytes_avg": int(nbytes), "block_copies": n_copies,
-           "us_per_block_stats": stats(per_step, 1e6 / len(order), 2)}
+           "us_per_block_stats": stats(per_step, 1e6 / len(order), 2),
+           "expert_path": "grouped MFMA GEMM" if M * k >= 4 * E else "matrix-core expert GEMV"}
     out.update(roofline(nbytes, flops, per))
     if not extras:
         del moes, packed, batches
@@ -870,7 +884,7 @@ PMC_PASSES = [
     "FETCH_SIZE",
     "WRITE_SIZE",
 ]
-N_CU, N_SIMD = 256, 4
+N_CU, N_SIMD, N_XCC = 256, 4, 8
 
 
 def pmc_summary(case, kernel, out_path, dirs):
@@ -892,9 +906,17 @@ def pmc_summary(case, kernel, out_path, dirs):
                 key = (f, r["Dispatch_Id"], r["Counter_Name"])
                 vals.setdefault(key, []).append(float(r["Counter_Value"]))
     per = {}
+    durs = {}
     for (_, disp, cname), v in vals.items():
-        # per-instance rows: block counters add up, the GPU-wide cycle count is the largest
-        per.setdefault(cname, []).append(max(v) if cname.startswith("GRBM_") else sum(v))
+        # one row per dispatch and counter, summed over the counter's instances
+        # (shader engines, XCDs): GRBM_GUI_ACTIVE is then the sum of the 8
+        # XCDs' busy cycles
+        per.setdefault(cname, []).append(sum(v))
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if kernel in r["Kernel_Name"]:
+                    durs[(f, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
     mean = {c: float(np.mean(v)) for c, v in per.items()}
     n = {c: len(v) for c, v in per.items()}
     lines = [f"rocprofv3 counters of {kernel} in 'python3 bench.py --case {case}' (per-dispatch means)", "",
@@ -906,12 +928,13 @@ def pmc_summary(case, kernel, out_path, dirs):
     for c in sorted(mean):
         lines.append(f"  {c:28s} {mean[c]:18.1f}  (n={n[c]})")
     lines.append("")
+    if durs:
+        lines.append(f"dispatch duration under counter collection: {float(np.mean(list(durs.values()))):.2f} us "
+                     f"(mean over {len(durs)} dispatches of all passes)")
     gui = mean.get("GRBM_GUI_ACTIVE")
     if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
-        lines.append(f"matrix-core busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {N_CU} CUs x {N_SIMD} SIMDs) = "
-                     f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * N_CU * N_SIMD):.4f}")
-    if gui and "SQ_BUSY_CYCLES" in mean:
-        lines.append(f"SQ busy: SQ_BUSY_CYCLES / GRBM_GUI_ACTIVE = {mean['SQ_BUSY_CYCLES'] / gui:.3f}")
+        lines.append(f"matrix-core busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCC} XCDs x {N_CU} CUs x "
+                     f"{N_SIMD} SIMDs) = {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui / N_XCC * N_CU * N_SIMD):.4f}")
     if mean.get("SQ_INSTS_MFMA"):
         lines.append(f"VALU instructions per MFMA instruction: {mean.get('SQ_INSTS_VALU', 0) / mean['SQ_INSTS_MFMA']:.2f}")
     if mean.get("SQ_INSTS_LDS"):
@@ -929,7 +952,9 @@ def pmc_summary(case, kernel, out_path, dirs):
         lines.append(f"HBM bytes per dispatch (scaled): "
                      f"{mean['FETCH_SIZE'] * 1024 * 2.0 + mean.get('WRITE_SIZE', 0.0) * 1024:.0f}")
     lines.append("")
-    lines.append("kernels seen: " + ", ".join(sorted(k[:60] for k in names))[:2000])
+    srcs = next((v for k, v in KERNEL_SOURCES.items() if k in kernel), None)
+    if srcs:
+        lines.append(f"@source_hash: {source_hash(srcs)}  ({', '.join(os.path.basename(p) for p in srcs)})")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -968,7 +993,8 @@ def planes_meta_bytes(k, n, bits):
 
 # ---------------------------------------------------------------- main
 
-CASES = ("stack1", "stack4", "stack16", "single", "ffn1", "ffn8", "ffn64", "ffn256", "pvq1", "pvq16", "pvq64", "moe")
+CASES = ("stack1", "stack4", "stack16", "single", "ffn1", "ffn8", "ffn64", "ffn256", "pvq1", "pvq16", "pvq64", "moe",
+         "moe256", "moe2048")
 
 
 def run_case(torch, L, case, steps):
@@ -983,7 +1009,7 @@ def run_case(torch, L, case, steps):
     elif case.startswith("pvq"):
         r = extra_pvq(torch, L, steps, Ms=(int(case[3:]),))
     else:
-        r = extra_moe(torch, L, steps, extras=False)
+        r = extra_moe(torch, L, steps, extras=False, M=int(case[3:]) if len(case) > 3 else None)
     print(json.dumps({"case": case, "result": r}), flush=True)
 
 
@@ -1113,6 +1139,9 @@ def main():
         extra["pvq"] = extra_pvq(torch, L, steps)
         log("[bench] extra: MoE block")
         extra["moe_block"] = extra_moe(torch, L, steps)
+        for M in (256, 2048):
+            log(f"[bench] extra: MoE block, {M} tokens (prefill)")
+            extra[f"moe_block_M{M}"] = extra_moe(torch, L, max(3, steps // 2), extras=False, M=M)
         m64 = extra["ffn_pair"]["M64"]
         extra["TFLOPs_at_M64"] = {"value": m64["TFLOPs"], "frac_of_mfma_peak": round(m64["TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
                                   "workload": "FFN pair 5120->17408 (2-bit) + 17408->5120 (3-bit), M=64"}

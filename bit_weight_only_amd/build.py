@@ -42,32 +42,53 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source and link liblbq.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+# host-side sanitizers (address, undefined behaviour) for the checking build:
+# applied to the host pass only, the GPU code is built as usual
+SAN_HOST = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+LIB_SANITIZED = os.path.join(PKG, "_build_san", "liblbq_san.so")
+
+
+def build(verbose: bool = False, jobs: int | None = None, sanitize: bool = False) -> str:
+    """Compile every source and link liblbq.so; returns the library path.
+
+    sanitize=True builds _build_san/liblbq_san.so instead: every host-side
+    part (the packers, the argument checks and launch code of the C ABI) under
+    AddressSanitizer and UndefinedBehaviorSanitizer, all of it with the ROCm
+    clang so one sanitizer runtime serves the process (load it with LD_PRELOAD
+    of clang's libclang_rt.asan-x86_64.so and point LBQ_LIBRARY at the file).
+    """
+    bdir = os.path.join(PKG, "_build_san") if sanitize else BUILD
+    os.makedirs(bdir, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
     cmds = []
     objs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        cmds.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(bdir, src + ".o")
+        san = [f for flag in SAN_HOST for f in ("-Xarch_host", flag)] if sanitize else []
+        cmds.append([HIPCC, *HIP_FLAGS, *san, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        cmds.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(bdir, src + ".o")
+        if sanitize:
+            clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang++")
+            cmds.append([clang, *HOST_FLAGS, *SAN_HOST, "-c", os.path.join(CSRC, src), "-o", obj])
+        else:
+            cmds.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with cf.ThreadPoolExecutor(jobs) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-pthread"])
-    os.replace(tmp, LIB)
+    lib = LIB_SANITIZED if sanitize else LIB
+    tmp = lib + ".tmp"
+    link_san = ["-shared-libsan", *[f for flag in SAN_HOST[:1] for f in ("-Xarch_host", flag)]] if sanitize else []
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_san, "-o", tmp, *objs, "-pthread"])
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
     sys.exit(0)

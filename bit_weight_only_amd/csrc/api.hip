@@ -23,7 +23,7 @@ inline lbq_status hip_status(hipError_t e) { return e == hipSuccess ? LBQ_OK : L
 lbq_status check_weight(const lbq_weight *w) {
   if (!w || !w->planes || !w->meta || !w->signs) return LBQ_ERR_NULL;
   if (w->format == LBQ_FMT_RTN_PLANES) {
-    if (w->bits < 2 || w->bits > 4) return LBQ_ERR_BITS;
+    if ((w->bits < 2 || w->bits > 4) && w->bits != 8) return LBQ_ERR_BITS;
   } else if (w->format == LBQ_FMT_PVQ_4x8) {
     if (!w->codebook) return LBQ_ERR_NULL;
     if (w->bits != 2) return LBQ_ERR_BITS;
@@ -36,7 +36,7 @@ lbq_status check_weight(const lbq_weight *w) {
 }
 
 GemmPlan linear_gemm_plan(const lbq_weight *w, int M) {
-  return w->format == LBQ_FMT_RTN_PLANES ? gemm_rtn_plan(M, w->K, w->N) : gemm_plan(M, w->K, w->N);
+  return w->format == LBQ_FMT_RTN_PLANES ? gemm_rtn_plan(M, w->K, w->N, w->bits) : gemm_plan(M, w->K, w->N);
 }
 
 size_t tz_bytes(const lbq_weight *w, int M) {
@@ -66,9 +66,10 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
   if (ws_bytes < linear_ws_bytes(w, M)) return LBQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // up to four tokens share one matrix-core GEMV pass; from there on the MFMA GEMM
-  const bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 4);
+  bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 4);
   // One to four tokens: rotation fused into the matrix-core decoder, one launch.
-  if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_mfma_supported(M, w->K, w->N) && aligned16(w->signs))
+  if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_mfma_supported(M, w->K, w->N) && aligned16(w->signs) &&
+      (w->bits != 8 || gemv_mfma_supported_8bit(w->K, w->N)))
     return hip_status(launch_gemv_mfma(w->planes, w->meta, x, w->signs, y, M, w->K, w->N, w->bits, 0, 0, 0, s, ev0,
                                        ev1));
   if (w->format == LBQ_FMT_PVQ_4x8 && gemv && gemv_pvq_mx_supported(M, w->K, w->N) && aligned16(w->signs) &&
@@ -80,6 +81,11 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
     return (ev1 && hipEventRecord(ev1, s) != hipSuccess) ? LBQ_ERR_HIP : LBQ_OK;
   }
   uint16_t *xr = static_cast<uint16_t *>(ws);
+  // 8-bit codes run on the matrix-core GEMV or the MFMA GEMM only
+  if (gemv && w->format == LBQ_FMT_RTN_PLANES && w->bits == 8) {
+    if (path == LBQ_PATH_GEMV) return LBQ_ERR_SHAPE;
+    gemv = false;
+  }
   if (!gemv) {
     // MFMA GEMM: rotation into the folded order (with the RTN zero-point sums,
     // clearing the split-K counters), then the GEMM
@@ -135,7 +141,7 @@ lbq_status lbq_packed_bytes(int32_t K, int32_t N, int32_t bits, int32_t format, 
                             size_t *meta_bytes) {
   if (!plane_bytes || !meta_bytes) return LBQ_ERR_NULL;
   if (format == LBQ_FMT_RTN_PLANES) {
-    if (bits < 2 || bits > 4) return LBQ_ERR_BITS;
+    if ((bits < 2 || bits > 4) && bits != 8) return LBQ_ERR_BITS;
   } else if (format == LBQ_FMT_PVQ_4x8) {
     if (bits != 2) return LBQ_ERR_BITS;
   } else {
@@ -308,7 +314,7 @@ lbq_status lbq_rotate(const uint16_t *x, int32_t M, int32_t K, const int8_t *sig
 namespace {
 
 struct MoeLayout {
-  size_t xr, ids, weights, counts, offsets, perm, act, out, h, total;
+  size_t xr, ids, weights, counts, offsets, perm, act, out, h, tz_h, tz_f, tiles, n_tiles, total;
 };
 
 MoeLayout moe_layout(const lbq_moe *m, int M) {
@@ -329,6 +335,10 @@ MoeLayout moe_layout(const lbq_moe *m, int M) {
   L.act = take(mk * m->ffn * 2);
   L.out = take(mk * m->hidden * 4);
   L.h = take(mk * m->ffn * 2 * 4);
+  L.tz_h = take(static_cast<size_t>(M) * gemm_tz_stride(m->hidden) * 4);
+  L.tz_f = take(mk * gemm_tz_stride(m->ffn) * 4);
+  L.tiles = take(static_cast<size_t>(moe_prefill_max_tiles(M, m->E, m->top_k)) * 16);
+  L.n_tiles = take(4);
   L.total = off;
   return L;
 }
@@ -358,10 +368,16 @@ lbq_status lbq_moe_workspace(const lbq_moe *m, int32_t M, size_t *bytes) {
   return LBQ_OK;
 }
 
-lbq_status lbq_moe_forward(const lbq_moe *m, const uint16_t *x, const float *logits, int32_t M, uint16_t *y,
-                           void *ws, size_t ws_bytes, void *stream) {
+lbq_status lbq_moe_forward_path(const lbq_moe *m, const uint16_t *x, const float *logits, int32_t M, uint16_t *y,
+                                void *ws, size_t ws_bytes, int32_t path, void *stream) {
   lbq_status st = check_moe(m, M);
   if (st != LBQ_OK) return st;
+  if (path < LBQ_PATH_AUTO || path > LBQ_PATH_GEMM) return LBQ_ERR_SHAPE;
+  const long assignments = static_cast<long>(M) * m->top_k;
+  const bool grouped_ok = moe_prefill_supported(m->hidden, m->ffn, assignments);
+  if (path == LBQ_PATH_GEMM && !grouped_ok) return LBQ_ERR_SHAPE;
+  // the grouped GEMMs once the experts see about four tokens each on average
+  const bool grouped = path == LBQ_PATH_GEMM || (path == LBQ_PATH_AUTO && grouped_ok && assignments >= 4L * m->E);
   if (M == 0) return LBQ_OK;
   if (!x || !logits || !y || !ws) return LBQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return LBQ_ERR_ALIGN;
@@ -400,7 +416,20 @@ lbq_status lbq_moe_forward(const lbq_moe *m, const uint16_t *x, const float *log
   a.y = y;
   if (launch_moe_route(logits, M, m->E, m->top_k, ids, wts, counts, offsets, perm, s) != hipSuccess)
     return LBQ_ERR_HIP;
+  if (grouped) {
+    MoePrefill p{};
+    p.tiles = reinterpret_cast<int32_t *>(base + L.tiles);
+    p.n_tiles = reinterpret_cast<int32_t *>(base + L.n_tiles);
+    p.tz_hidden = reinterpret_cast<uint32_t *>(base + L.tz_h);
+    p.tz_ffn = reinterpret_cast<uint32_t *>(base + L.tz_f);
+    return hip_status(launch_moe_prefill(a, p, s));
+  }
   return hip_status(launch_moe_experts(a, s));
+}
+
+lbq_status lbq_moe_forward(const lbq_moe *m, const uint16_t *x, const float *logits, int32_t M, uint16_t *y,
+                           void *ws, size_t ws_bytes, void *stream) {
+  return lbq_moe_forward_path(m, x, logits, M, y, ws, ws_bytes, LBQ_PATH_AUTO, stream);
 }
 
 lbq_status lbq_moe_route(const float *logits, int32_t M, int32_t E, int32_t top_k, int32_t *ids, float *weights,

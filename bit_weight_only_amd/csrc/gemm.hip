@@ -311,17 +311,19 @@ GemmPlan gemm_plan(int M, int K, int N) {
   return p;
 }
 
-GemmPlan gemm_rtn_plan(int M, int K, int N) {
+GemmPlan gemm_rtn_plan(int M, int K, int N, int bits) {
   // Measured on the dense-stack and FFN shapes (K up to 17408, N 4096..28672,
   // M 8..256). Up to 32 tokens the loop is bound by each compute unit's
   // vector-memory address path: one row block per wave, and K split until
   // about 384 workgroups run, every slice keeping at least eight groups. From
   // 33 tokens two row blocks per wave (each activation fragment read from LDS
   // feeds two MFMAs; one for rows of >= 64 groups below 128 tokens), four once
-  // that alone gives >= 384 workgroups, and K split
-  // until 256 workgroups run (512 for rows of >= 64 groups at >= 128 tokens),
-  // slices of at least sixteen groups: split-K partial tiles go through
-  // device-coherent memory and cost more than a partly idle chip.
+  // that alone gives >= 384 workgroups (two for 8-bit codes: registers for
+  // their planes), and K split until 256 workgroups run (512 for rows of >= 64
+  // groups at >= 128 tokens), slices of at least sixteen groups: split-K
+  // partial tiles go through device-coherent memory and cost more than a
+  // partly idle chip. (Sweeps of 32-token tiles and of more workgroups at 64
+  // and 256 tokens were faster back to back but not under graph replay.)
   GemmPlan p;
   p.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   const int G = K / kGroup;
@@ -335,7 +337,7 @@ GemmPlan gemm_rtn_plan(int M, int K, int N) {
   } else {
     const long t4 = static_cast<long>((N + 255) / 256) * p.m_tiles;
     // long rows below 128 tokens: one block per wave, the split carries the chip
-    p.nb = t4 >= 384 ? 4 : (G >= 64 && M < 128) ? 1 : 2;
+    p.nb = (t4 >= 384 && bits != 8) ? 4 : (G >= 64 && M < 128) ? 1 : 2;
     p.n_tiles = (N + 64 * p.nb - 1) / (64 * p.nb);
     const long tiles = static_cast<long>(p.n_tiles) * p.m_tiles;
     const long target = (G >= 64 && M >= 128) ? 512 : 256;

@@ -50,7 +50,11 @@ constexpr int kThreads = 64 * kWaves;
 // Ring slots: loads run kRing - 1 groups ahead. Deeper rings measured no
 // faster: at few tokens the loop is bound by the compute unit's vector-memory
 // address path (about one 128-byte line per few cycles), not by latency.
-constexpr int kRing = 3;
+#ifndef LBQ_GEMM_RING
+#define LBQ_GEMM_RING 3
+#endif
+constexpr int kRing = LBQ_GEMM_RING;
+static_assert(kRing >= 3 && kRing <= 8, "ring depth");
 constexpr int kBufferFlags = 0x00020000;        // buffer descriptor word 3 (32-bit data, no swizzle)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every supported size
 
@@ -67,13 +71,30 @@ __host__ __device__ constexpr int meta_vectors(int ns) {
 struct RtnGemmArgs {
   const uint4 *xf;         // rotated activations [M][K] fp16, folded slot order
   const uint4 *tz;         // [M][Gp / 4] of 4 u32: (T/16 high, T/16 low) fp16 per (token, group)
-  const uint4 *planes;     // [N][G][BITS] 16-byte plane vectors
-  const uint32_t *meta;    // [N][G] (fp16 s, fp16 z)
+  const uint4 *planes;     // [N][G][BITS] 16-byte plane vectors (grouped: base of all experts' planes)
+  const uint32_t *meta;    // [N][G] (fp16 s, fp16 z) (grouped: base of all experts' meta)
   uint16_t *y;             // [M][N]
   float *part;             // split-K partial tiles (S > 1)
   uint32_t *counters;      // split-K arrival counters, one per tile, zero on entry
   int M, K, N, S, Gp;
   int MS;                  // LDS row stride (words) of the staged scale/zero words: 4 vectors + 1
+  // grouped GEMM over routed experts (gemm_rtn_grouped_kernel): a workgroup's
+  // token tile is entries i0 .. i0 + cnt - 1 of the expert-sorted assignment
+  // list, all routed to one expert e, whose weight sits at the byte offsets
+  // plane_off[e] / meta_off[e]
+  const int4 *tiles;       // [max tiles] (e, i0, cnt, bits), from moe_tiles
+  const int32_t *n_tiles;  // tiles in use
+  const uint64_t *plane_off, *meta_off;
+  const int32_t *perm;     // list entry -> assignment index t * top_k + j
+  int act_div;             // activation row of entry i: perm[i] / act_div, or i when 0
+  int out_perm;            // output row of entry i: perm[i] when 1, else i
+  float *out;              // fp32 outputs [rows][N]
+};
+
+// The token tile of one workgroup: dense, tokens m0 .. m0 + 16 MT - 1 of x;
+// grouped, entries i0 .. i0 + cnt - 1 of the assignment list.
+struct TokenTile {
+  int m0, i0, cnt;
 };
 
 __device__ __forceinline__ uint32_t pk_fma(uint32_t h, half2_t s2, half2_t c) {
@@ -84,7 +105,8 @@ __device__ __forceinline__ uint32_t pk_fma(uint32_t h, half2_t s2, half2_t c) {
 // word; fields 2..4 sit at mantissa bits 4, 6, 8, fields 5..7 land there after
 // a shift right by 6 and fields 0, 1 at bits 4, 6 after a shift left by 4.
 // Class index (m - 4) / 2. 3/4-bit: nibble i of the merged nibble words, moved
-// to bits 4..7 (class 0, m = 4) by a shift of 4 - 4i.
+// to bits 4..7 (class 0, m = 4) by a shift of 4 - 4i. 8-bit: the low nibble at
+// bits 2..5 and the high nibble at bits 6..9 (one class, m = 2).
 template <int BITS>
 __host__ __device__ constexpr int gemm_slot_class(int c) {
   if constexpr (BITS == 2) {
@@ -97,6 +119,11 @@ __host__ __device__ constexpr int gemm_slot_class(int c) {
 template <int BITS>
 constexpr int gemm_num_classes() {
   return BITS == 2 ? 3 : 1;
+}
+// The offset 2^(10 - m) of class c (the decode removes s times it).
+template <int BITS>
+__host__ __device__ constexpr float gemm_class_offset(int c) {
+  return BITS == 8 ? 256.0f : static_cast<float>(1 << (6 - 2 * c));
 }
 
 // Biased decode of one 32-code word column into the 16 slots (fp16 pairs
@@ -124,6 +151,20 @@ __device__ __forceinline__ void decode_biased(const uint32_t *w, uint32_t h[16])
     h[13] = and_or(orr, 0x00C000C0u, c6);
     h[14] = and_or(er, 0x03000300u, c8);
     h[15] = and_or(orr, 0x03000300u, c8);
+  } else if constexpr (BITS == 8) {
+    // nibble i of lo[r] / hi[r] is the low / high half of code 4i + r; slot
+    // 4p + r takes nibbles p (low half of the slot) and p + 4 (high half)
+    uint32_t lo[4], hi[4];
+    merge_nibbles<4>(w, lo);
+    merge_nibbles<4>(w + 4, hi);
+    const uint32_t c2 = biased_one2(2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      h[r] = and_or(hi[r] << 6, 0x03C003C0u, and_or(lo[r] << 2, 0x003C003Cu, c2));
+      h[4 + r] = and_or(hi[r] << 2, 0x03C003C0u, and_or(lo[r] >> 2, 0x003C003Cu, c2));
+      h[8 + r] = and_or(hi[r] >> 2, 0x03C003C0u, and_or(lo[r] >> 6, 0x003C003Cu, c2));
+      h[12 + r] = and_or(hi[r] >> 6, 0x03C003C0u, and_or(lo[r] >> 10, 0x003C003Cu, c2));
+    }
   } else {
     uint32_t n[4];
     merge_nibbles<BITS>(w, n);
@@ -138,10 +179,10 @@ __device__ __forceinline__ void decode_biased(const uint32_t *w, uint32_t h[16])
   }
 }
 
-// The ring slots are separate LDS objects so the compiler can tell that a read
-// of one slot does not depend on the copies in flight into the others.
-template <int BITS, int NB, int MT>
-__global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
+// One workgroup's tile: the mainloop shared by the dense and the grouped GEMM.
+template <int BITS, int NB, int MT, bool GROUPED>
+__device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 *planes, const uint32_t *meta,
+                                              const TokenTile tt, uint4 *const *xs, uint32_t *msm) {
   constexpr int U = NB * BITS;           // 16-byte plane vectors of a wave's rows per group
   constexpr int T = (U + 3) / 4;         // of them per lane
   constexpr int D = kRing - 1;           // groups in flight
@@ -150,11 +191,7 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
   constexpr int kRowsWG = kWaves * 16 * NB;
   constexpr int kMetaIters = (kRowsWG * meta_vectors(meta_max_groups(NB)) + kThreads - 1) / kThreads;
   constexpr int C = gemm_num_classes<BITS>();
-  __shared__ __attribute__((aligned(16))) uint4 xs0[16 * MT * 16];
-  __shared__ __attribute__((aligned(16))) uint4 xs1[16 * MT * 16];
-  __shared__ __attribute__((aligned(16))) uint4 xs2[16 * MT * 16];
-  uint4 *const xs[kRing] = {xs0, xs1, xs2};
-  extern __shared__ uint32_t msm[];   // [kRowsWG][a.MS]: (s, z) of group gb0 + c at column c
+  // msm: [kRowsWG][a.MS] (s, z) of group gb0 + c at column c; xs: the ring slots
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -163,14 +200,24 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
   const int split = blockIdx.x;
   const int tile_id = blockIdx.z * gridDim.y + blockIdx.y;
   const int row0 = blockIdx.y * (kWaves * 16 * NB) + wave * 16 * NB + j;   // the lane's row of block 0
-  const int m0 = blockIdx.z * (16 * MT);
   const int g0 = static_cast<int>((static_cast<long>(split) * G) / a.S);
   const int g1 = static_cast<int>((static_cast<long>(split + 1) * G) / a.S);
 
+  const int m0 = tt.m0;
   const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint4 *>(a.planes), 0, a.N * G * BITS * 16, kBufferFlags);
+      const_cast<uint4 *>(planes), 0, a.N * G * BITS * 16, kBufferFlags);
   const __amdgpu_buffer_rsrc_t mrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(a.meta), 0, a.N * G * 4, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(meta), 0, a.N * G * 4, kBufferFlags);
+  // x / tz row of token slot tok of the tile (slots past the tile repeat its
+  // last token; their outputs are never stored)
+  auto act_row = [&](int tok) -> size_t {
+    if constexpr (GROUPED) {
+      const int i = tt.i0 + min(tok, tt.cnt - 1);
+      return static_cast<size_t>(a.act_div ? a.perm[i] / a.act_div : i);
+    } else {
+      return static_cast<size_t>(min(m0 + tok, a.M - 1));
+    }
+  };
 
   // lane (j, kq) loads plane vectors u = kq + 4t of its rows: block u / BITS, plane u % BITS
   uint32_t poff[T];
@@ -203,7 +250,7 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
   for (int i = 0; i < CA; ++i) {
     const int p = 64 * (CA * wave + i) + lane;
     const int tok = p >> 4, c = (p & 15) ^ (tok & 15);
-    asrc[i] = a.xf + static_cast<size_t>(min(m0 + tok, a.M - 1)) * (a.K / 8) + c;
+    asrc[i] = a.xf + act_row(tok) * (a.K / 8) + c;
   }
 
   uint4 bv[kRing][T];
@@ -256,7 +303,7 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
       s2[nb] = half2_t{s, s};
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        const _Float16 off = static_cast<_Float16>(-static_cast<float>(1 << (6 - 2 * c)));   // -2^(10 - m)
+        const _Float16 off = static_cast<_Float16>(-gemm_class_offset<BITS>(c));   // -2^(10 - m)
         nc[nb][c] = s2[nb] * half2_t{off, off};
       }
       decode_biased<BITS>(&w[nb * BITS], h[nb]);
@@ -311,8 +358,7 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
     half8_t za[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int tok = min(m0 + mt * 16 + j, a.M - 1);
-      za[mt] = __builtin_bit_cast(half8_t, a.tz[static_cast<size_t>(tok) * (a.Gp / 4) + 4 * c16 + kq]);
+      za[mt] = __builtin_bit_cast(half8_t, a.tz[act_row(mt * 16 + j) * (a.Gp / 4) + 4 * c16 + kq]);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -332,6 +378,26 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
   }
   wait_vm_lds<0>();   // no copy into LDS may outlive the workgroup
 
+  if constexpr (GROUPED) {
+    // fp32 results by output row of each list entry (no split-K here)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = mt * 16 + kq * 4 + r;
+        if (tok < tt.cnt) {
+          const int i = tt.i0 + tok;
+          float *orow = a.out + static_cast<size_t>(a.out_perm ? a.perm[i] : i) * a.N;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int row = row0 + nb * 16;
+            if (row < a.N) orow[row] = acc[nb][mt][r];
+          }
+        }
+      }
+    }
+    return;
+  }
   if (a.S > 1) {
     // publish this slice's partial tile; the last slice to arrive sums them all
     constexpr int kTileFloats = NB * MT * 4 * kThreads;
@@ -384,6 +450,43 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
   }
 }
 
+// The ring slots are separate LDS objects so the compiler can tell that a read
+// of one slot does not depend on the copies in flight into the others.
+#define LBQ_RING_SLOTS(MT)                                                                              \
+  __shared__ __attribute__((aligned(16))) uint4 xs0[16 * (MT) * 16];                                    \
+  __shared__ __attribute__((aligned(16))) uint4 xs1[16 * (MT) * 16];                                    \
+  __shared__ __attribute__((aligned(16))) uint4 xs2[kRing > 2 ? 16 * (MT) * 16 : 1];                   \
+  __shared__ __attribute__((aligned(16))) uint4 xs3[kRing > 3 ? 16 * (MT) * 16 : 1];                   \
+  __shared__ __attribute__((aligned(16))) uint4 xs4[kRing > 4 ? 16 * (MT) * 16 : 1];                   \
+  __shared__ __attribute__((aligned(16))) uint4 xs5[kRing > 5 ? 16 * (MT) * 16 : 1];                   \
+  __shared__ __attribute__((aligned(16))) uint4 xs6[kRing > 6 ? 16 * (MT) * 16 : 1];                   \
+  __shared__ __attribute__((aligned(16))) uint4 xs7[kRing > 7 ? 16 * (MT) * 16 : 1];                   \
+  uint4 *const xs[8] = {xs0, xs1, xs2, xs3, xs4, xs5, xs6, xs7};                                        \
+  extern __shared__ uint32_t msm[];
+
+template <int BITS, int NB, int MT>
+__global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
+  LBQ_RING_SLOTS(MT)
+  gemm_rtn_body<BITS, NB, MT, false>(a, a.planes, a.meta, TokenTile{static_cast<int>(blockIdx.z) * 16 * MT, 0, 0}, xs,
+                                     msm);
+}
+
+// Grouped GEMM over routed experts: workgroup (., y, z) takes row tile y of
+// the expert of tile descriptor z, at that expert's own code width.
+template <int NB, int MT>
+__global__ void __launch_bounds__(kThreads) gemm_rtn_grouped_kernel(RtnGemmArgs a) {
+  if (static_cast<int>(blockIdx.z) >= *a.n_tiles) return;
+  LBQ_RING_SLOTS(MT)
+  const int4 d = a.tiles[blockIdx.z];   // (e, i0, cnt, bits)
+  const uint4 *pl = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(a.planes) + a.plane_off[d.x]);
+  const uint32_t *mt = reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(a.meta) + a.meta_off[d.x]);
+  const TokenTile tt{0, d.y, d.z};
+  if (d.w == 2) gemm_rtn_body<2, NB, MT, true>(a, pl, mt, tt, xs, msm);
+  else if (d.w == 3) gemm_rtn_body<3, NB, MT, true>(a, pl, mt, tt, xs, msm);
+  else gemm_rtn_body<4, NB, MT, true>(a, pl, mt, tt, xs, msm);
+}
+#undef LBQ_RING_SLOTS
+
 template <int BITS, int NB, int MT>
 hipError_t launch_rtn(dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
   const size_t lds = static_cast<size_t>(kWaves * 16 * NB) * a.MS * 4;
@@ -400,10 +503,11 @@ hipError_t launch_rtn(dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
 
 template <int BITS>
 hipError_t launch_rtn_bits(const GemmPlan &p, dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
-  if (p.nb == 4) {
-    if (p.mt == 1) return launch_rtn<BITS, 4, 1>(grid, a, s);
-    if (p.mt == 2) return launch_rtn<BITS, 4, 2>(grid, a, s);
-    return launch_rtn<BITS, 4, 4>(grid, a, s);
+  if (BITS != 8 && p.nb == 4) {
+    constexpr int NB4 = BITS == 8 ? 2 : 4;   // (8-bit codes: no four-block plans)
+    if (p.mt == 1) return launch_rtn<BITS, NB4, 1>(grid, a, s);
+    if (p.mt == 2) return launch_rtn<BITS, NB4, 2>(grid, a, s);
+    return launch_rtn<BITS, NB4, 4>(grid, a, s);
   }
   if (p.nb == 2) {
     if (p.mt == 1) return launch_rtn<BITS, 2, 1>(grid, a, s);
@@ -421,6 +525,45 @@ int gemm_rtn_meta_max_groups(int nb) {
   return meta_max_groups(nb);
 }
 
+hipError_t launch_gemm_rtn_grouped(const GroupedGemm &g, hipStream_t s) {
+  if (g.max_tiles <= 0) return hipSuccess;
+  if ((g.nb != 1 && g.nb != 2) || (g.mt != 1 && g.mt != 2 && g.mt != 4)) return hipErrorInvalidValue;
+  const int G = g.K / kGroup;
+  if (g.K % kGroup != 0 || G > meta_max_groups(g.nb) || g.max_tiles > 65535) return hipErrorInvalidValue;
+  RtnGemmArgs a{};
+  a.xf = reinterpret_cast<const uint4 *>(g.xf);
+  a.tz = reinterpret_cast<const uint4 *>(g.tz);
+  a.planes = static_cast<const uint4 *>(g.planes);
+  a.meta = static_cast<const uint32_t *>(g.meta);
+  a.K = g.K;
+  a.N = g.N;
+  a.S = 1;
+  a.Gp = gemm_tz_stride(g.K);
+  a.MS = 4 * meta_vectors(G) + 1;
+  a.tiles = reinterpret_cast<const int4 *>(g.tiles);
+  a.n_tiles = g.n_tiles;
+  a.plane_off = g.plane_off;
+  a.meta_off = g.meta_off;
+  a.perm = g.perm;
+  a.act_div = g.act_div;
+  a.out_perm = g.out_perm;
+  a.out = g.out;
+  const dim3 grid(1, static_cast<unsigned>((g.N + 64 * g.nb - 1) / (64 * g.nb)), static_cast<unsigned>(g.max_tiles));
+  const size_t lds = static_cast<size_t>(kWaves * 16 * g.nb) * a.MS * 4;
+  auto kern = g.nb == 1 ? (g.mt == 1 ? gemm_rtn_grouped_kernel<1, 1> : g.mt == 2 ? gemm_rtn_grouped_kernel<1, 2>
+                                                                                  : gemm_rtn_grouped_kernel<1, 4>)
+                        : (g.mt == 1 ? gemm_rtn_grouped_kernel<2, 1> : g.mt == 2 ? gemm_rtn_grouped_kernel<2, 2>
+                                                                                  : gemm_rtn_grouped_kernel<2, 4>);
+  const size_t ring = static_cast<size_t>(kRing) * 16 * g.mt * 16 * 16;
+  if (ring + lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
 int gemm_tz_stride(int K) {
   return (K / kGroup + 15) / 16 * 16;
 }
@@ -435,7 +578,8 @@ hipError_t launch_gemm_rtn(const GemmPlan &p, int bits, const void *planes, cons
   if (M <= 0) return hipSuccess;
   if ((p.nb != 1 && p.nb != 2 && p.nb != 4) || (p.mt != 1 && p.mt != 2 && p.mt != 4) || p.S < 1)
     return hipErrorInvalidValue;
-  if (bits < 2 || bits > 4 || !gemm_rtn_supported(K, N, bits)) return hipErrorInvalidValue;
+  if ((bits < 2 || bits > 4) && bits != 8) return hipErrorInvalidValue;
+  if (!gemm_rtn_supported(K, N, bits) || (bits == 8 && p.nb > 2)) return hipErrorInvalidValue;
   const int G = K / kGroup, ns = (G + p.S - 1) / p.S;   // longest slice
   if (p.S > G || ns > meta_max_groups(p.nb)) return hipErrorInvalidValue;
   RtnGemmArgs a;
@@ -456,7 +600,8 @@ hipError_t launch_gemm_rtn(const GemmPlan &p, int bits, const void *planes, cons
   switch (bits) {
     case 2: return launch_rtn_bits<2>(p, grid, a, s);
     case 3: return launch_rtn_bits<3>(p, grid, a, s);
-    default: return launch_rtn_bits<4>(p, grid, a, s);
+    case 4: return launch_rtn_bits<4>(p, grid, a, s);
+    default: return launch_rtn_bits<8>(p, grid, a, s);
   }
 }
 

@@ -287,7 +287,18 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
                         static_cast<int>(lo[3]), 0, 0, 0, 0};
       acc[u] = v4f_t{0.f, 0.f, 0.f, 0.f};
       acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bl, acc[u], 0, 4, 0, 127, 0, 127);
-      if constexpr (BITS > 2) {
+      if constexpr (BITS == 8) {
+        // q = q0 + 4 q1 + 16 q2 + 64 q3, 2-bit digits from plane pairs (2d, 2d + 1),
+        // digit d on the matrix cores with the B scale 2^(2d)
+#pragma unroll
+        for (int d = 1; d < 4; ++d) {
+          uint32_t dg[4];
+          fp4_from_pair(pl[2 * d], pl[2 * d + 1], dg);
+          const v8i_t bd = {static_cast<int>(dg[0]), static_cast<int>(dg[1]), static_cast<int>(dg[2]),
+                            static_cast<int>(dg[3]), 0, 0, 0, 0};
+          acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bd, acc[u], 0, 4, 0, 127, 0, 127 + 2 * d);
+        }
+      } else if constexpr (BITS > 2) {
         uint32_t hi[4];
         if constexpr (BITS == 3) fp4_from_single(pl[2], hi);
         else fp4_from_pair(pl[2], pl[3], hi);
@@ -423,7 +434,12 @@ void gemv_mfma_shape(int M, int K, int N, int bits, int &grid, int &block, int &
   while (grid < T && tokens_per_pass(M, G, padded_groups(G, 3), ((T + grid - 1) / grid) * 16, block / 64) == 0)
     grid = grid * 2 < T ? grid * 2 : T;
   // ring depth: a third slot pays once each wave streams several tiles or long rows
-  depth = bits == 3 ? 2 : (bits == 4 || T >= 4 * kComputeUnits || G >= 64) ? 3 : 2;
+  depth = bits == 3 ? 2 : (bits >= 4 || T >= 4 * kComputeUnits || G >= 64) ? 3 : 2;
+}
+
+bool gemv_mfma_supported_8bit(int K, int N) {
+  // buffer offsets are 32-bit and kOutOfRange must lie past the planes of 8-bit codes
+  return static_cast<long long>(N + 16) * (K / kGroup) * 8 * 16 < static_cast<long long>(kOutOfRange);
 }
 
 bool gemv_mfma_supported(int M, int K, int N) {
@@ -442,7 +458,8 @@ hipError_t launch_gemv_mfma(const void *planes, const void *meta, const uint16_t
                             hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   if (M < 1 || M > 4 || (reinterpret_cast<uintptr_t>(signs) & 15u) != 0 || (reinterpret_cast<uintptr_t>(x) & 15u) != 0)
     return hipErrorInvalidValue;
-  if (bits < 2 || bits > 4 || !gemv_mfma_supported(M, K, N)) return hipErrorInvalidValue;
+  if ((bits < 2 || bits > 4) && bits != 8) return hipErrorInvalidValue;
+  if (!gemv_mfma_supported(M, K, N) || (bits == 8 && !gemv_mfma_supported_8bit(K, N))) return hipErrorInvalidValue;
   int g0, b0, d0;
   gemv_mfma_shape(M, K, N, bits, g0, b0, d0);
   if (grid <= 0) grid = g0;
@@ -455,7 +472,8 @@ hipError_t launch_gemv_mfma(const void *planes, const void *meta, const uint16_t
   switch (bits) {
     case 2: return launch_bits<2>(planes, meta, x, signs, y, sh, grid, block, depth, mp, s, start, stop);
     case 3: return launch_bits<3>(planes, meta, x, signs, y, sh, grid, block, depth, mp, s, start, stop);
-    default: return launch_bits<4>(planes, meta, x, signs, y, sh, grid, block, depth, mp, s, start, stop);
+    case 4: return launch_bits<4>(planes, meta, x, signs, y, sh, grid, block, depth, mp, s, start, stop);
+    default: return launch_bits<8>(planes, meta, x, signs, y, sh, grid, block, depth, mp, s, start, stop);
   }
 }
 

@@ -18,6 +18,13 @@ hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, u
 hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, uint32_t *tz,
                                 uint32_t *counters, int n_counters, hipStream_t s, int max_tokens = 0);
 
+// The routed experts' SwiGLU intermediate, rotated into the folded order: row
+// m of out is R (fp16(silu(h[m][0..K-1]) h[m][K..2K-1])), with the RTN GEMM's
+// zero-point sums in tz (as launch_rotate_folded). h: fp32 [M][2K], M * 2K *
+// 4 bytes below 2 GiB.
+hipError_t launch_swiglu_rotate_folded(const float *h, int M, int K, const int8_t *signs, uint16_t *out,
+                                       uint32_t *tz, hipStream_t s);
+
 // RTN dequant-GEMV for 1 <= M <= 16 on already-rotated activations xr [M][K].
 hipError_t launch_gemv_rtn(const void *planes, const void *meta, const uint16_t *xr, uint16_t *y, int M, int K,
                            int N, int bits, hipStream_t s);
@@ -28,6 +35,7 @@ hipError_t launch_gemv_rtn(const void *planes, const void *meta, const uint16_t 
 // grid / block / depth <= 0 take gemv_mfma_shape's choice; non-null events
 // take the kernel's own begin / end times.
 bool gemv_mfma_supported(int M, int K, int N);
+bool gemv_mfma_supported_8bit(int K, int N);   // the extra bound for 8-bit codes
 void gemv_mfma_shape(int M, int K, int N, int bits, int &grid, int &block, int &depth);
 hipError_t launch_gemv_mfma(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs,
                             uint16_t *y, int M, int K, int N, int bits, int grid, int block, int depth,
@@ -55,7 +63,7 @@ struct GemmPlan {
   int nb, mt, S, n_tiles, m_tiles;
 };
 GemmPlan gemm_plan(int M, int K, int N);
-GemmPlan gemm_rtn_plan(int M, int K, int N);
+GemmPlan gemm_rtn_plan(int M, int K, int N, int bits);
 // longest K slice (groups) whose scale/zero words the RTN GEMM stages in LDS,
 // for nb row blocks per wave; launch_gemm_rtn rejects plans with longer slices
 int gemm_rtn_meta_max_groups(int nb);
@@ -66,6 +74,26 @@ int gemm_tz_stride(int K);
 bool gemm_rtn_supported(int K, int N, int bits);
 hipError_t launch_gemm_rtn(const GemmPlan &p, int bits, const void *planes, const void *meta, const uint16_t *xf,
                            const uint32_t *tz, uint16_t *y, int M, int K, int N, void *scratch, hipStream_t s);
+// Grouped RTN GEMM over routed experts: for each tile descriptor (e, i0, cnt,
+// bits) the rows of list entries i0 .. i0 + cnt - 1 (activation row of entry i:
+// perm[i] / act_div, or i when act_div is 0) times expert e's weight (byte
+// offsets plane_off[e] / meta_off[e] from planes / meta, width bits), fp32
+// results to out[(out_perm ? perm[i] : i)][N]. Row tiles of 64 nb, token tiles
+// of 16 mt entries (cnt <= 16 mt); grid over max_tiles descriptors, those past
+// *n_tiles exit at once.
+struct GroupedGemm {
+  int nb, mt, max_tiles, K, N;
+  const int32_t *tiles;      // [max_tiles] int4 descriptors
+  const int32_t *n_tiles;
+  const void *planes, *meta;
+  const uint64_t *plane_off, *meta_off;
+  const uint16_t *xf;        // folded rotated activations, rows of K
+  const uint32_t *tz;        // zero-point sums, rows of gemm_tz_stride(K)
+  const int32_t *perm;
+  int act_div, out_perm;
+  float *out;
+};
+hipError_t launch_gemm_rtn_grouped(const GroupedGemm &g, hipStream_t s);
 hipError_t launch_gemm_pvq(const GemmPlan &p, const void *idx, const void *row_scale, const uint8_t *codebook,
                            const uint16_t *xf, uint16_t *y, int M, int K, int N, void *scratch, hipStream_t s);
 
@@ -88,8 +116,8 @@ struct MoeArgs {
   const uint8_t *planes, *meta;
   const int8_t *signs_hidden, *signs_ffn;
   const uint16_t *x;         // [M][hidden] tokens
-  const uint16_t *xr;        // [M][hidden] rotated tokens (VALU expert kernels)
-  float *h;                  // [M*top_k][2*ffn] gate|up results (matrix-core expert kernels)
+  const uint16_t *xr;        // [M][hidden] rotated tokens (VALU expert kernels; folded for the grouped GEMMs)
+  float *h;                  // [M*top_k][2*ffn] gate|up results (matrix-core expert kernels and grouped GEMMs)
   const int32_t *offsets;    // [E+1]
   const int32_t *perm;       // [M*top_k]
   const float *weights;      // [M][top_k]
@@ -99,6 +127,21 @@ struct MoeArgs {
 };
 // Rotation (VALU path), expert linears and the weighted combine.
 hipError_t launch_moe_experts(const MoeArgs &a, hipStream_t s);
+// Many tokens per expert: the expert linears as grouped MFMA GEMMs over the
+// expert-sorted assignment list (after the router): tile descriptors, the
+// tokens rotated once (xr, folded, sums in tz_hidden), gate|up into h (fp32,
+// list order), SwiGLU + ffn rotation into act (folded, sums in tz_ffn), down
+// into out (by assignment index), the combine.
+struct MoePrefill {
+  int32_t *tiles;        // [moe_prefill_max_tiles] int4
+  int32_t *n_tiles;
+  uint32_t *tz_hidden;   // [M][gemm_tz_stride(hidden)]
+  uint32_t *tz_ffn;      // [M * top_k][gemm_tz_stride(ffn)]
+};
+int moe_prefill_tile_tokens(int M, int E, int top_k);
+int moe_prefill_max_tiles(int M, int E, int top_k);
+bool moe_prefill_supported(int hidden, int ffn, long assignments);
+hipError_t launch_moe_prefill(const MoeArgs &a, const MoePrefill &p, hipStream_t s);
 // Expert linears on the matrix cores (gate|up, SwiGLU, down; rotations fused).
 bool moe_mx_supported(int hidden, int ffn, const int8_t *signs_hidden, const int8_t *signs_ffn);
 hipError_t launch_moe_mx(const MoeArgs &a, hipStream_t s);
@@ -106,7 +149,7 @@ hipError_t launch_moe_mx(const MoeArgs &a, hipStream_t s);
 size_t moe_gateup_lds(int hidden);
 size_t moe_down_lds(int ffn);
 constexpr int kMoeMaxExperts = 1024;
-constexpr int kMoeMaxAssignments = 8192;
+constexpr int kMoeMaxAssignments = 1 << 20;
 constexpr int kMoeMaxTopK = 32;
 
 }  // namespace lbq

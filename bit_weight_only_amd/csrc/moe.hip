@@ -29,7 +29,6 @@ namespace {
 
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxExperts = 1024;
-constexpr int kMaxAssignments = 8192;
 constexpr int kMaxTokChunk = 8;
 
 // ------------------------------------------------------------------ router
@@ -150,7 +149,6 @@ __global__ void __launch_bounds__(kRouteThreads) moe_sort_kernel(const int32_t *
                                                                   int32_t *__restrict__ offsets,
                                                                   int32_t *__restrict__ perm) {
   constexpr int kWaves = kRouteThreads / 64;
-  __shared__ int32_t s_ids[kMaxAssignments];
   __shared__ int32_t s_cnt[kWaves * kMaxExperts];   // per (token chunk, expert): count, then run start
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // 2. counting sort of the assignments by expert, stable in the assignment
@@ -162,11 +160,11 @@ __global__ void __launch_bounds__(kRouteThreads) moe_sort_kernel(const int32_t *
   const int MK = M * top_k;
   const int chunk = (M + kWaves - 1) / kWaves;
   const int t_lo = min(M, wave * chunk), t_hi = min(M, t_lo + chunk);
+  (void)MK;
   for (int i = threadIdx.x; i < kWaves * E; i += kRouteThreads) s_cnt[i] = 0;
-  for (int a = threadIdx.x; a < MK; a += kRouteThreads) s_ids[a] = ids[a];
   __syncthreads();
   for (int t = t_lo; t < t_hi; ++t)
-    if (lane < top_k) s_cnt[wave * E + s_ids[t * top_k + lane]] += 1;
+    if (lane < top_k) s_cnt[wave * E + ids[t * top_k + lane]] += 1;
   __syncthreads();
   // exclusive offsets: thread i owns experts kPerThread i .. kPerThread (i + 1) - 1;
   // scan of the per-thread totals within each wave, then across the waves
@@ -216,7 +214,7 @@ __global__ void __launch_bounds__(kRouteThreads) moe_sort_kernel(const int32_t *
   for (int t = t_lo; t < t_hi; ++t)
     if (lane < top_k) {
       const int a = t * top_k + lane;
-      perm[s_cnt[wave * E + s_ids[a]]++] = a;
+      perm[s_cnt[wave * E + ids[a]]++] = a;
     }
 }
 
@@ -420,11 +418,109 @@ hipError_t launch_moe_route(const float *logits, int M, int E, int top_k, int32_
   return hipGetLastError();
 }
 
+// Tile descriptors of the grouped expert GEMMs: expert e's list entries
+// [offsets[e], offsets[e + 1]) in tiles of `per`, each (e, first entry,
+// entries, bits[e]), experts in id order; *n_tiles = their number. One
+// workgroup, one expert per thread.
+__global__ void __launch_bounds__(kRouteThreads) moe_tiles_kernel(const int32_t *__restrict__ offsets,
+                                                                   const uint8_t *__restrict__ bits, int E, int per,
+                                                                   int4 *__restrict__ tiles,
+                                                                   int32_t *__restrict__ n_tiles) {
+  constexpr int kWaves = kRouteThreads / 64;
+  __shared__ int32_t s_wave[kWaves];
+  const int e = threadIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int first = e < E ? offsets[e] : 0;
+  const int cnt = e < E ? offsets[e + 1] - first : 0;
+  const int nt = (cnt + per - 1) / per;
+  int incl = nt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int start = incl - nt;
+  for (int w = 0; w < wave; ++w) start += s_wave[w];
+  for (int k = 0; k < nt; ++k)
+    tiles[start + k] = make_int4(e, first + k * per, min(per, cnt - k * per), e < E ? bits[e] : 0);
+  if (threadIdx.x == kRouteThreads - 1) *n_tiles = start + nt;
+}
+
 size_t moe_gateup_lds(int hidden) {
   const int G = hidden / kGroup;
   return static_cast<size_t>(kMaxTokChunk) * G * kStagedGroupBytes + 2 * kGuRows * kMaxTokChunk * sizeof(float);
 }
 size_t moe_down_lds(int ffn) { return static_cast<size_t>(kMaxTokChunk) * (ffn / kGroup) * kStagedGroupBytes; }
+
+int moe_prefill_tile_tokens(int M, int E, int top_k) {
+  const long avg = (static_cast<long>(M) * top_k + E - 1) / E;   // list entries per expert
+  return avg <= 16 ? 16 : avg <= 32 ? 32 : 64;
+}
+
+int moe_prefill_max_tiles(int M, int E, int top_k) {
+  const int per = moe_prefill_tile_tokens(M, E, top_k);
+  return static_cast<int>((static_cast<long>(M) * top_k + per - 1) / per) + E;
+}
+
+bool moe_prefill_supported(int hidden, int ffn, long assignments) {
+  // the grouped GEMM stages a row tile's scale/zero words for the whole K in
+  // LDS (two 16-row blocks per wave up to 40 groups), h is read through 32-bit
+  // offsets
+  return hidden / kGroup <= gemm_rtn_meta_max_groups(2) && ffn / kGroup <= gemm_rtn_meta_max_groups(2) &&
+         assignments * 2 * ffn * 4 < (1L << 31);
+}
+
+hipError_t launch_moe_prefill(const MoeArgs &a, const MoePrefill &p, hipStream_t s) {
+  const int per = moe_prefill_tile_tokens(a.M, a.E, a.top_k);
+  const int max_tiles = moe_prefill_max_tiles(a.M, a.E, a.top_k);
+  const int A = a.M * a.top_k;
+  hipLaunchKernelGGL(moe_tiles_kernel, dim3(1), dim3(kRouteThreads), 0, s, a.offsets, a.bits, a.E, per,
+                     reinterpret_cast<int4 *>(p.tiles), p.n_tiles);
+  hipError_t e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // tokens rotated once with the hidden signs (folded order, zero-point sums)
+  if ((e = launch_rotate_folded(a.x, a.M, a.hidden, a.signs_hidden, const_cast<uint16_t *>(a.xr), p.tz_hidden,
+                                nullptr, 0, s)) != hipSuccess)
+    return e;
+  GroupedGemm g{};
+  g.nb = 2;
+  g.mt = per / 16;
+  g.max_tiles = max_tiles;
+  g.tiles = p.tiles;
+  g.n_tiles = p.n_tiles;
+  g.planes = a.planes;
+  g.meta = a.meta;
+  g.perm = a.perm;
+  // gate|up: token rows perm[i] / top_k, results in list order
+  g.K = a.hidden;
+  g.N = 2 * a.ffn;
+  g.plane_off = a.gu_plane_off;
+  g.meta_off = a.gu_meta_off;
+  g.xf = a.xr;
+  g.tz = p.tz_hidden;
+  g.act_div = a.top_k;
+  g.out_perm = 0;
+  g.out = a.h;
+  if ((e = launch_gemm_rtn_grouped(g, s)) != hipSuccess) return e;
+  // SwiGLU, fp16, rotated with the ffn signs, in list order
+  if ((e = launch_swiglu_rotate_folded(a.h, A, a.ffn, a.signs_ffn, a.act, p.tz_ffn, s)) != hipSuccess) return e;
+  // down: rows in list order, results by assignment index for the combine
+  g.K = a.ffn;
+  g.N = a.hidden;
+  g.plane_off = a.dn_plane_off;
+  g.meta_off = a.dn_meta_off;
+  g.xf = a.act;
+  g.tz = p.tz_ffn;
+  g.act_div = 0;
+  g.out_perm = 1;
+  g.out = a.out;
+  if ((e = launch_gemm_rtn_grouped(g, s)) != hipSuccess) return e;
+  const long total = static_cast<long>(a.M) * a.hidden;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, a.out,
+                     a.weights, a.M, a.hidden, a.top_k, a.y);
+  return hipGetLastError();
+}
 
 hipError_t launch_moe_experts(const MoeArgs &a, hipStream_t s) {
   hipError_t e;

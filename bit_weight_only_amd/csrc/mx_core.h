@@ -64,6 +64,10 @@ template <>
 struct MxBatch<4> {
   static constexpr int GB = 1, NV = 1;
 };
+template <>
+struct MxBatch<8> {
+  static constexpr int GB = 1, NV = 2;   // one group of eight planes: 128 bytes per row
+};
 
 template <int BITS>
 struct MxItem {
@@ -293,14 +297,17 @@ struct MxCursor {
 };
 
 // Groups padded to whole batches of the code width.
+inline int batch_groups(int bits) {
+  return bits == 2 ? MxBatch<2>::GB : bits == 3 ? MxBatch<3>::GB : bits == 4 ? MxBatch<4>::GB : MxBatch<8>::GB;
+}
 inline int padded_groups(int G, int bits) {
-  const int gb = bits == 2 ? MxBatch<2>::GB : bits == 3 ? MxBatch<3>::GB : MxBatch<4>::GB;
+  const int gb = batch_groups(bits);
   return (G + gb - 1) / gb * gb;
 }
 
 inline MxShape make_shape(int M, int K, int N, int bits, int grid, int block) {
   MxShape sh;
-  const int gb = bits == 2 ? MxBatch<2>::GB : bits == 3 ? MxBatch<3>::GB : MxBatch<4>::GB;
+  const int gb = batch_groups(bits);
   sh.M = M;
   sh.K = K;
   sh.N = N;

@@ -157,7 +157,9 @@ bool group_scale(const double *u, int stride, int bits, uint16_t &s16, double &s
   }
   const double L = static_cast<double>((1 << bits) - 1);
   s16 = f64_to_f16_rne((mx - mn) / L);
-  if ((s16 & 0x7FFFu) >= 0x5800u) return false;   // s >= 128 (or not finite)
+  // the MFMA GEMM's fp16 decode constants (-64 s, -16 s z; -256 s and
+  // -16 s z with z up to 255 at 8 bits) must stay finite: s < 128, at 8 bits s < 16
+  if ((s16 & 0x7FFFu) >= (bits == 8 ? 0x4C00u : 0x5800u)) return false;
   if (s16 == 0) s16 = 0x3C00u;                     // degenerate group: scale 1
   s = f16_to_f64(s16);
   z = std::rint(-mn / s) + 0.0;

@@ -49,7 +49,13 @@ __global__ void __launch_bounds__(256) rotate_kernel(const uint32_t *__restrict_
 // shuffles for the butterflies and six more for the sum). Lane L holds the
 // 16-value half L & 1 of chunk L >> 1; the even and odd lanes of a chunk swap
 // half their values with one DPP move each, and each writes eight whole slots.
-__global__ void __launch_bounds__(256) rotate_folded_kernel(const uint32_t *__restrict__ x,
+//
+// With SWIGLU the rows are not read from x but formed from fp32 gate|up
+// results h [M][2K] (gate in columns 0..K-1, up in K..2K-1): the value at k is
+// silu(h[m][k]) h[m][K + k] rounded to fp16, the routed experts' SwiGLU
+// intermediate, rotated with the ffn signs for their down linear.
+template <bool SWIGLU>
+__global__ void __launch_bounds__(256) rotate_folded_kernel(const uint32_t *__restrict__ x, const float *__restrict__ h,
                                                             const int8_t *__restrict__ signs,
                                                             uint32_t *__restrict__ out, uint32_t *__restrict__ tz,
                                                             int M, int K, int Gp, uint32_t *__restrict__ counters,
@@ -63,10 +69,44 @@ __global__ void __launch_bounds__(256) rotate_folded_kernel(const uint32_t *__re
   const int m = ok ? static_cast<int>(unit / G) : 0, g = ok ? static_cast<int>(unit - static_cast<long>(m) * G) : 0;
   // buffer loads: lanes without a unit load zeros (every lane takes part in the
   // DPP exchanges below)
-  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(x), 0,
-                                                                        M * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(signs), 0, K, 0x00020000);
-  const mx::RotIn in = mx::rot_load(xrs, srs, K, m, g, L, ok);
+  mx::RotIn in;
+  if constexpr (SWIGLU) {
+    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(h), 0, M * K * 8,
+                                                                          0x00020000);
+    const uint32_t bad = ok ? 0u : mx::kOutOfRange;
+    const uint32_t go = static_cast<uint32_t>((m * 2 * K + g * kGroup + 16 * L) * 4) + bad;
+    const uint32_t uo = go + static_cast<uint32_t>(K * 4);
+    float gv[16], uv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(hrs, go + 16 * q, 0, 0));
+      const float4 c = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(hrs, uo + 16 * q, 0, 0));
+      gv[4 * q] = a.x;
+      gv[4 * q + 1] = a.y;
+      gv[4 * q + 2] = a.z;
+      gv[4 * q + 3] = a.w;
+      uv[4 * q] = c.x;
+      uv[4 * q + 1] = c.y;
+      uv[4 * q + 2] = c.z;
+      uv[4 * q + 3] = c.w;
+    }
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a0 = gv[2 * i] / (1.f + __expf(-gv[2 * i])) * uv[2 * i];
+      const float a1 = gv[2 * i + 1] / (1.f + __expf(-gv[2 * i + 1])) * uv[2 * i + 1];
+      w[i] = static_cast<uint32_t>(f32_to_f16_bits(a0)) | (static_cast<uint32_t>(f32_to_f16_bits(a1)) << 16);
+    }
+    in.xa = make_uint4(w[0], w[1], w[2], w[3]);
+    in.xb = make_uint4(w[4], w[5], w[6], w[7]);
+    in.sv = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(srs, static_cast<uint32_t>(g * kGroup + 16 * L) + bad, 0, 0));
+  } else {
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(x), 0,
+                                                                          M * K * 2, 0x00020000);
+    in = mx::rot_load(xrs, srs, K, m, g, L, ok);
+  }
   float v[16];
   {
     const uint32_t xw[8] = {in.xa.x, in.xa.y, in.xa.z, in.xa.w, in.xb.x, in.xb.y, in.xb.z, in.xb.w};
@@ -137,6 +177,17 @@ __global__ void __launch_bounds__(256) rotate_folded_kernel(const uint32_t *__re
     for (int gz = G + L; gz < Gp; gz += 8) row[gz] = 0;
 }
 
+hipError_t launch_swiglu_rotate_folded(const float *h, int M, int K, const int8_t *signs, uint16_t *out,
+                                       uint32_t *tz, hipStream_t s) {
+  // 32 (row, group) units per workgroup; h is read through 32-bit buffer
+  // offsets (M * 2K floats stay below 2 GiB: checked by the caller)
+  const long nblk = static_cast<long>(M) * (K / kGroup);
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(rotate_folded_kernel<true>, dim3(static_cast<unsigned>((nblk + 31) / 32)), dim3(256), 0, s,
+                     nullptr, h, signs, reinterpret_cast<uint32_t *>(out), tz, M, K, gemm_tz_stride(K), nullptr, 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, uint32_t *tz,
                                 uint32_t *counters, int n_counters, hipStream_t s, int max_tokens) {
   // 32 (token, group) units per workgroup; buffer offsets are 32-bit, so the
@@ -152,8 +203,8 @@ hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *s
     const int nc = m0 == 0 ? n_counters : 0;
     const long need = std::max<long>((nblk + 31) / 32, (nc + 255) / 256);
     if (need > 0)
-      hipLaunchKernelGGL(rotate_folded_kernel, dim3(static_cast<unsigned>(need)), dim3(256), 0, s,
-                         reinterpret_cast<const uint32_t *>(x + static_cast<long>(m0) * K), signs,
+      hipLaunchKernelGGL(rotate_folded_kernel<false>, dim3(static_cast<unsigned>(need)), dim3(256), 0, s,
+                         reinterpret_cast<const uint32_t *>(x + static_cast<long>(m0) * K), nullptr, signs,
                          reinterpret_cast<uint32_t *>(out + static_cast<long>(m0) * K),
                          tz ? tz + static_cast<long>(m0) * Gp : nullptr, Mc, K, Gp, counters, nc);
     m0 += Mc;

@@ -31,6 +31,16 @@ __global__ void __launch_bounds__(256) unpack_rtn_kernel(const uint32_t *__restr
       out[2 * f] = static_cast<uint8_t>((e >> (2 * f)) & 3u);
       out[2 * f + 1] = static_cast<uint8_t>((o >> (2 * f)) & 3u);
     }
+  } else if constexpr (BITS == 8) {
+    // the GEMM's route: nibble words of planes 0..3 and 4..7
+    uint32_t lo[4], hi[4];
+    merge_nibbles<4>(p, lo);
+    merge_nibbles<4>(p + 4, hi);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        out[4 * i + r] = static_cast<uint8_t>(((lo[r] >> (4 * i)) & 15u) | (((hi[r] >> (4 * i)) & 15u) << 4));
   } else {
     uint32_t n[4];
     merge_nibbles<BITS>(p, n);
@@ -58,7 +68,8 @@ hipError_t launch_unpack_rtn(const void *planes, int K, int N, int bits, uint8_t
   switch (bits) {
     case 2: hipLaunchKernelGGL(unpack_rtn_kernel<2>, dim3(grid), dim3(256), 0, s, pl, out, columns); break;
     case 3: hipLaunchKernelGGL(unpack_rtn_kernel<3>, dim3(grid), dim3(256), 0, s, pl, out, columns); break;
-    default: hipLaunchKernelGGL(unpack_rtn_kernel<4>, dim3(grid), dim3(256), 0, s, pl, out, columns); break;
+    case 4: hipLaunchKernelGGL(unpack_rtn_kernel<4>, dim3(grid), dim3(256), 0, s, pl, out, columns); break;
+    default: hipLaunchKernelGGL(unpack_rtn_kernel<8>, dim3(grid), dim3(256), 0, s, pl, out, columns); break;
   }
   return hipGetLastError();
 }

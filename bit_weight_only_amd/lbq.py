@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblbq.so")
+# LBQ_LIBRARY may name another build of the same library (the sanitizer build)
+LIB_PATH = os.environ.get("LBQ_LIBRARY") or os.path.join(_HERE, "liblbq.so")
 
 FMT_RTN_PLANES = 0
 FMT_PVQ_4x8 = 1
@@ -30,7 +31,7 @@ EXPORTS = [
     "lbq_status_string", "lbq_packed_bytes", "lbq_pack", "lbq_linear_workspace", "lbq_linear_forward",
     "lbq_linear_forward_path", "lbq_linear_forward_timed", "lbq_moe_workspace", "lbq_moe_forward", "lbq_moe_route", "lbq_unpack_codes",
     "lbq_rotate", "lbq_linear_forward_noalloc", "lbq_stream_read", "lbq_gptq_factor",
-    "lbq_pack_gptq",
+    "lbq_pack_gptq", "lbq_moe_forward_path",
 ]
 
 
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.lbq_linear_forward_timed.argtypes = [ctypes.POINTER(Weight), c_vp, c_i32, c_vp, c_vp, c_sz, c_vp, c_vp, c_vp]
         L.lbq_moe_workspace.argtypes = [ctypes.POINTER(Moe), c_i32, p_sz]
         L.lbq_moe_forward.argtypes = [ctypes.POINTER(Moe), c_vp, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]
+        L.lbq_moe_forward_path.argtypes = [ctypes.POINTER(Moe), c_vp, c_vp, c_i32, c_vp, c_vp, c_sz, c_i32, c_vp]
         L.lbq_moe_route.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
         L.lbq_unpack_codes.argtypes = [ctypes.POINTER(Weight), c_vp, c_vp]
         L.lbq_rotate.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]
@@ -261,7 +263,7 @@ class PackedMoe:
         return b.value
 
 
-def moe_forward(m: PackedMoe, x, logits, y=None, ws=None, stream=None):
+def moe_forward(m: PackedMoe, x, logits, y=None, ws=None, path: int = PATH_AUTO, stream=None):
     import torch
 
     M = int(x.shape[0])
@@ -269,8 +271,8 @@ def moe_forward(m: PackedMoe, x, logits, y=None, ws=None, stream=None):
         y = torch.empty((M, m.hidden), dtype=torch.float16, device=x.device)
     if ws is None:
         ws = torch.empty(max(1, m.workspace_bytes(M)), dtype=torch.uint8, device=x.device)
-    st = lib().lbq_moe_forward(ctypes.byref(m.struct), _ptr(x), _ptr(logits), M, _ptr(y), _ptr(ws), ws.numel(),
-                               _stream(stream))
+    st = lib().lbq_moe_forward_path(ctypes.byref(m.struct), _ptr(x), _ptr(logits), M, _ptr(y), _ptr(ws), ws.numel(),
+                                    int(path), _stream(stream))
     _check(st, "lbq_moe_forward")
     return y
 

@@ -269,10 +269,22 @@ lbq_status lbq_moe_workspace(const lbq_moe *m, int32_t M, size_t *bytes);
  * y_t = sum_j w_tj o_tj, summed in fp32 in slot order, written fp16.
  *   x: fp16 [M][hidden]; logits: fp32 [M][E]; y: fp16 [M][hidden] (device,
  *   16-byte aligned); ws: lbq_moe_workspace(m, M) bytes.
- * Limits: E <= 1024, top_k <= 32, M * top_k <= 8192 (LBQ_ERR_SHAPE). Errors
+ * Limits: E <= 1024, top_k <= 32, M * top_k <= 2^20 (LBQ_ERR_SHAPE). Errors
  * as lbq_linear_forward. */
 lbq_status lbq_moe_forward(const lbq_moe *m, const uint16_t *x, const float *logits, int32_t M,
                            uint16_t *y, void *ws, size_t ws_bytes, void *stream);
+
+/* lbq_moe_forward with an explicit path for the expert linears: LBQ_PATH_GEMV
+ * (the matrix-core expert GEMVs, tokens of an expert in chunks of four) or
+ * LBQ_PATH_GEMM (grouped MFMA dequant-GEMMs over the expert-sorted assignment
+ * list, with the codes decoded inside the mainloop rather than expanded to a
+ * dense copy first: the prefill gap the Laguna-S-2.1 card names in "Reading it
+ * honestly"). AUTO takes the GEMMs once M * top_k >= 4 E (about four tokens per
+ * expert). The GEMM path needs hidden and ffn of at most 5120 and
+ * M * top_k * ffn * 8 below 2^31 (LBQ_ERR_SHAPE otherwise). Same operation,
+ * arguments and errors as lbq_moe_forward. */
+lbq_status lbq_moe_forward_path(const lbq_moe *m, const uint16_t *x, const float *logits, int32_t M,
+                                uint16_t *y, void *ws, size_t ws_bytes, int32_t path, void *stream);
 
 /* Router pass alone (the first step of lbq_moe_forward; Laguna-S-2.1 card,
  * base-model line: 256 routed experts, top-k per token), for inspection:

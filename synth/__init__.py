@@ -75,6 +75,31 @@ def codebook(workload: int = 0, item: int = 0, entries: int = 256, dim: int = 4)
         it += 1000
 
 
+# the NVFP4 (e2m1) value grid, non-negative half; as e4m3 bytes
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+def codebook_fp4(workload: int = 0, item: int = 0, entries: int = 256, dim: int = 4) -> np.ndarray:
+    """[entries][dim] codebook whose values lie on the NVFP4 (e2m1) grid,
+    stored as fp8 e4m3 bytes (every e2m1 value is exact in e4m3). Entries are
+    2 x N(0,1) draws moved to the nearest grid value (ties to the smaller
+    magnitude); draws repeat with the next item until the entries are distinct."""
+    import torch
+
+    it = item
+    while True:
+        g = rng(workload, it, ROLE_CODEBOOK)
+        v = 2.0 * g.standard_normal((entries, dim), dtype=np.float32)
+        mag = np.abs(v)
+        pick = np.argmin(np.abs(mag[..., None] - E2M1_VALUES), axis=-1)   # first (smaller) of equals
+        q = np.sign(v) * E2M1_VALUES[pick]
+        b = torch.from_numpy(q.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        b[q == 0] = 0   # +0 for every zero
+        if len(np.unique(b.view(np.dtype((np.void, dim))))) == entries:
+            return b
+        it += 1000
+
+
 ROLE_CALIB = 6
 
 

@@ -57,7 +57,7 @@ def test_packed_bytes(L):
     assert lib.lbq_packed_bytes(128, 4, 2, 0, None, ctypes.byref(b)) == -1
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("n,k", [(1, 128), (3, 256), (130, 512), (64, 1152)])
 def test_host_pack_is_byte_identical_to_oracle(L, bits, n, k):
     w = synth.weights(n, k, workload=8, item=bits * 1000 + n)
@@ -83,6 +83,20 @@ def test_pack_rejects_rtn_scales_from_128(L):
     with pytest.raises(L.LbqError) as e:
         L.pack(w * 8000.0, 2, s)
     assert e.value.status == -6
+
+
+def test_pack_rejects_8bit_scales_from_16(L):
+    """At 8 bits the GEMM's decode holds -256 s and -16 s z (z up to 255) in
+    fp16, so the packer refuses group scales of 16 or more (weights 2000 times
+    the usual size give 8-bit scales near 0.6, accepted)."""
+    s = synth.signs(256, workload=8, item=9)
+    w = synth.weights(4, 256, workload=8, item=9)
+    _, meta = L.pack(w * 2000.0, 8, s)
+    assert np.frombuffer(meta.tobytes(), dtype=np.float16)[0::2].astype(np.float64).max() < 16
+    with pytest.raises(L.LbqError) as e:
+        L.pack(w * 60000.0, 8, s)
+    assert e.value.status == -6
+    assert L.packed_bytes(4096, 4096, 8) == (16777216, 524288)
 
 
 def test_host_pack_full_single_linear(L):
@@ -220,7 +234,7 @@ def test_moe_argument_errors(L):
     assert fwd(_moe(L, ffn=100)) == -2
     assert fwd(_moe(L, planes=FAKE + 1)) == -4
     assert fwd(m, M=-1) == -2
-    assert fwd(m, M=2000) == -2           # 2000 * 8 assignments exceed the limit
+    assert fwd(m, M=140000) == -2         # 140000 * 8 assignments exceed the limit of 2^20
     assert fwd(m, lg=0) == -1
     assert fwd(m, nb=1024) == -5
     assert fwd(m, M=0, x=0, lg=0, y=0, ws=0) == 0
@@ -283,7 +297,7 @@ def test_gptq_factor_matches_oracle(L, k):
     assert np.all(np.tril(u, -1) == 0.0)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_gptq_pack_byte_identical_given_the_same_factor(L, bits):
     """Given the same factor the host packer and the oracle take the same steps
     in the same order: identical planes and scale/zero words."""
@@ -339,3 +353,16 @@ def test_gptq_errors(L):
     with pytest.raises(L.LbqError) as e:
         L.pack_gptq(w, 2, s, u_bad)
     assert e.value.status == -6
+
+
+def test_host_pack_pvq_fp4_valued_codebook(L):
+    """Product-VQ against a codebook on the NVFP4 (e2m1) grid, held as e4m3
+    bytes: the host packer matches the oracle byte for byte."""
+    cb = synth.codebook_fp4(workload=synth.W_PVQ)
+    for n, k in [(5, 128), (64, 1024)]:
+        w = synth.weights(n, k, workload=8, item=100 + n)
+        s = synth.signs(k, workload=8, item=100 + n)
+        idx, sc = L.pack(w, 2, s, L.FMT_PVQ_4x8, cb)
+        oi, os_ = O.pack_pvq(w, s, cb)
+        assert np.array_equal(idx, oi.reshape(-1))
+        assert np.array_equal(sc, os_.view(np.uint8).reshape(-1))

@@ -306,3 +306,19 @@ def test_pvq_linear_sampled(L, dev, m):
     e = O.rel_l2(y[:, rows], want)
     say(f"  rel_l2={e:.3e}")
     assert e < TOL
+
+
+# ---------------------------------------------------------------- NVFP4-valued codebook
+
+@pytest.mark.parametrize("n,k", [(17, 512), (257, 1024), (130, 640)])
+@pytest.mark.parametrize("m,path", [(1, 1), (3, 1), (16, 1), (1, 2), (64, 2)])
+def test_pvq_fp4_valued_codebook(L, dev, n, k, m, path):
+    """The product-VQ decoders with a codebook whose values lie on the NVFP4
+    (e2m1) grid (held as e4m3 bytes): every path (the matrix-core GEMV at
+    K a multiple of 512 and up to four tokens, the VALU GEMV otherwise, the
+    MFMA GEMM) against the oracle."""
+    cb = synth.codebook_fp4(workload=16)
+    w, s, cb, idx, sc, pl = make_pvq(n, k, 16, 500 + n + k, cb=cb)
+    x = synth.activations(m, k, workload=16, item=500 + m)
+    y = L.linear_forward(pl, to_dev(x, dev), path=path).cpu().numpy().astype(np.float64)
+    assert O.rel_l2(y, oracle_pvq_rows(w, s, cb, x)) < TOL

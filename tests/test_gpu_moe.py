@@ -100,7 +100,9 @@ def test_moe_every_width_and_crowded_expert(L, dev, hidden, ffn):
     x = synth.activations(m, hidden, workload=18)
     lg = np.tile(np.array([[3.0, 2.0, 1.0, 0.0, -1.0, -2.0]], np.float32), (m, 1))
     lg[::4] = lg[::4][:, ::-1]
-    y = L.moe_forward(moe, to_dev(x, dev), to_dev(lg, dev)).cpu().numpy().astype(np.float64)
+    # 63 assignments over 6 experts would take the grouped GEMMs; the expert
+    # GEMV kernels are the ones under test here
+    y = L.moe_forward(moe, to_dev(x, dev), to_dev(lg, dev), path=L.PATH_GEMV).cpu().numpy().astype(np.float64)
     want = O.moe_forward(x, lg, top_k, _oracle_expert(w_gu, w_dn, bits, sh, sf, hidden, ffn))
     assert O.rel_l2(y, want) < TOL
 

@@ -590,3 +590,30 @@ def test_gptq_lowers_the_layer_output_error():
         loss_g = np.trace(e_g @ hr @ e_g.T)
         loss_r = np.trace(e_r @ hr @ e_r.T)
         assert loss_g < 0.8 * loss_r, (bits, loss_g / loss_r)
+
+
+def test_e2m1_grid_in_e4m3_and_fp4_codebook(golden_dir):
+    """The NVFP4-valued codebook: its e4m3 bytes decode to values of the e2m1
+    grid only (hand-derived encodings), its 256 entries are distinct, and the
+    product-VQ encoder's brute-force definition holds for it too."""
+    with open(os.path.join(golden_dir, "fp_formats.json")) as f:
+        g = json.load(f)["e2m1_in_e4m3"]
+    vals = O.e4m3_to_float(np.array(g["e4m3_bytes"], np.uint8))
+    assert list(vals) == g["values"]
+    grid = set(g["values"]) | {-v for v in g["values"]}
+    cb = synth.codebook_fp4(workload=4)
+    dec = O.e4m3_to_float(cb)
+    assert set(np.unique(dec).tolist()) <= grid
+    assert len(np.unique(cb.view(np.dtype((np.void, 4))))) == 256
+    # encode against the fp4-valued codebook by brute force on a small weight
+    s = synth.signs(128, workload=9, item=11)
+    w = synth.weights(3, 128, workload=9, item=11)
+    idx, sc = O.pack_pvq(w, s, cb)
+    wrot = O.rotate(w.astype(np.float64), s)
+    scale = sc.view(np.float16).astype(np.float64)
+    c = dec.reshape(256, 4)
+    for n in range(3):
+        for i in range(32):
+            a = wrot[n, 4 * i:4 * i + 4] / scale[n]
+            d = [(((a[0] - e[0]) ** 2 + (a[1] - e[1]) ** 2) + (a[2] - e[2]) ** 2) + (a[3] - e[3]) ** 2 for e in c]
+            assert idx[n, i] == int(np.argmin(d))
