@@ -24,6 +24,10 @@ What the pages fix, and where:
   paragraph).
 * Routed experts chosen per token (Laguna-S-2.1 card: 256 routed experts,
   top-k, plus the LLaDA2.2-mini card's routed experts).
+* Non-expert linears and the readout keep 8-bit codes, and the readout's codes
+  are also stored split into high and low nibble planes for a screened
+  readout (LLaDA2.2-mini card: property table, "Non-Expert Path" and
+  "Readout & Embeddings" rows, and the file list).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): Sylvester (natural) Hadamard order; signs applied before the
@@ -32,7 +36,10 @@ that always contains 0, integer zero-point, round-half-even; fp16-rounded scale
 used for code assignment; degenerate scale 0 -> 1; gate|up rows concatenated
 (gate first); SwiGLU expert activation; softmax over the selected top-k logits
 with ties broken toward the lower expert id; PVQ row scale by RMS matching and
-nearest-entry search with ties toward the lower index.
+nearest-entry search with ties toward the lower index; the screened readout
+scores every row by its high nibbles taken at the middle of their 16-code
+range, keeps a fixed number of rows per token (ties toward the lower row) and
+scores those exactly from both nibbles.
 """
 from __future__ import annotations
 
@@ -305,6 +312,58 @@ def split_nibbles(planes: np.ndarray) -> tuple:
     n = p.shape[0]
     p = p.reshape(n, -1, 8, 4)
     return np.ascontiguousarray(p[:, :, :4, :]), np.ascontiguousarray(p[:, :, 4:, :])
+
+
+def nibble_hi_meta(meta8: np.ndarray) -> np.ndarray:
+    """Scale/zero that make the high-nibble planes a 4-bit weight of their own
+    (reading of the LLaDA2.2-mini card's screened readout over the nibble-split
+    planes): with q = 16 h + l, the high nibble alone stands for the middle of
+    the 16 codes it spans, q ~ 16 h + 7.5, so s (q - z) ~ (16 s) (h - (z - 7.5) / 16).
+    meta8: uint16 [N][G][2] fp16 (s, z) of the 8-bit codes; returns the same
+    layout holding (16 s, (z - 7.5) / 16), both exact in fp16 for the 8-bit
+    packer's ranges (s < 16, integer z in 0..255)."""
+    m = np.asarray(meta8).view(np.uint16)
+    s = m[..., 0].copy().view(np.float16).astype(np.float64)
+    z = m[..., 1].copy().view(np.float16).astype(np.float64)
+    s_hi = 16.0 * s
+    z_hi = (z - 7.5) / 16.0
+    if not (np.all(to_fp16(s_hi).astype(np.float64) == s_hi) and np.all(to_fp16(z_hi).astype(np.float64) == z_hi)):
+        raise RangeError("high-nibble scale or zero not exact in fp16")
+    return pack_meta(to_fp16(s_hi), to_fp16(z_hi))
+
+
+def top_rows(values: np.ndarray, cand: int) -> np.ndarray:
+    """The `cand` largest entries of each row of values [M][N] (larger first,
+    ties to the lower index): int32 [M][cand]."""
+    v = np.asarray(values, dtype=np.float64)
+    m, n = v.shape
+    out = np.empty((m, cand), dtype=np.int32)
+    for t in range(m):
+        order = sorted(range(n), key=lambda i: (-v[t, i], i))
+        out[t] = order[:cand]
+    return out
+
+
+def screened_readout(x16, hi_planes, lo_planes, meta8, signs, n: int, k: int, cand: int):
+    """Screened readout over the nibble-split planes of an 8-bit weight.
+
+    1. coarse logits of every row from the high-nibble planes alone, read as
+       a 4-bit weight with nibble_hi_meta's scale and zero;
+    2. per token, the `cand` rows with the largest coarse logits (top_rows);
+    3. the exact logits of those rows from both nibbles, q = lo + 16 hi, with
+       the 8-bit (s, z).
+    Returns coarse float64 [M][N], ids int32 [M][cand], exact float64 [M][cand]."""
+    x = np.asarray(x16)
+    coarse = linear_rtn(x, hi_planes, nibble_hi_meta(meta8), signs, 4, n, k)
+    ids = top_rows(coarse, cand)
+    q = unpack_planes(lo_planes, 4, k).astype(np.uint16) + 16 * unpack_planes(hi_planes, 4, k).astype(np.uint16)
+    meta_rows = np.asarray(meta8).view(np.uint16).reshape(n, k // GROUP, 2)
+    exact = np.empty(ids.shape, dtype=np.float64)
+    for t in range(x.shape[0]):
+        rows = ids[t]
+        w_hat = dequant_weight_rtn(pack_planes(q[rows], 8), meta_rows[rows], signs, 8, len(rows), k)
+        exact[t] = linear(x[t:t + 1], w_hat)[0]
+    return coarse, ids, exact
 
 
 def pack_meta(s16: np.ndarray, z16: np.ndarray) -> np.ndarray:

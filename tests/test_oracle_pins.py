@@ -617,3 +617,59 @@ def test_e2m1_grid_in_e4m3_and_fp4_codebook(golden_dir):
             a = wrot[n, 4 * i:4 * i + 4] / scale[n]
             d = [(((a[0] - e[0]) ** 2 + (a[1] - e[1]) ** 2) + (a[2] - e[2]) ** 2) + (a[3] - e[3]) ** 2 for e in c]
             assert idx[n, i] == int(np.argmin(d))
+
+
+# ---------------------------------------------------------------- nibble-split screened readout
+
+def test_nibble_hi_meta_hand_values_and_split_identity():
+    """The high-nibble weight's (scale, zero): hand-derived values, and the
+    identity s (16 h + 7.5 - z) + s (l - 7.5) = s (q - z) through dequantize
+    of the two nibble weights against the 8-bit one (a lost midpoint or a
+    wrong factor of 16 fails it)."""
+    s = np.array([[0.0099945068359375, 2.0 ** -10, 15.5]], np.float16)
+    z = np.array([[37.0, 0.0, 255.0]], np.float16)
+    hi = O.nibble_hi_meta(O.pack_meta(s, z)).view(np.float16).astype(np.float64)
+    assert hi[0, :, 0].tolist() == [0.15991210937500, 2.0 ** -6, 248.0]
+    assert hi[0, :, 1].tolist() == [1.84375, -0.46875, 15.46875]
+    rng = np.random.default_rng(5)
+    n, k = 6, 384
+    q = rng.integers(0, 256, (n, k)).astype(np.uint8)
+    s8 = (rng.uniform(1e-4, 1e-2, (n, k // 128))).astype(np.float16)
+    z8 = rng.integers(0, 256, (n, k // 128)).astype(np.float16)
+    meta = O.pack_meta(s8, z8)
+    lo, hi_pl = O.split_nibbles(O.pack_planes(q, 8))
+    hs, hz = O.unpack_meta(O.nibble_hi_meta(meta), n, k)
+    coarse = O.dequantize(O.unpack_planes(hi_pl, 4, k), hs, hz)
+    rest = O.dequantize(O.unpack_planes(lo, 4, k), s8, np.full_like(z8, 7.5))
+    assert np.array_equal(coarse + rest, O.dequantize(q, s8, z8))
+
+
+def test_top_rows_against_library_sort_with_ties():
+    rng = np.random.default_rng(9)
+    v = rng.integers(-3, 4, (5, 40)).astype(np.float64)   # many ties
+    got = O.top_rows(v, 7)
+    for t in range(5):
+        want = np.lexsort((np.arange(40), -v[t]))[:7]
+        assert got[t].tolist() == want.tolist()
+
+
+def test_screened_readout_exact_on_candidates_and_coarse_bound():
+    """Exact logits of the screened rows equal the plain 8-bit readout's; every
+    coarse logit is within 7.5 sum_g s_g sum_k |x'_k| of the exact one (the low
+    nibble's largest deviation from its midpoint); the 8-bit argmax survives
+    the screen on this seeded case."""
+    n, k, m, cand = 300, 256, 3, 8
+    sg = synth.signs(k, workload=9, item=21)
+    w = synth.weights(n, k, workload=9, item=21)
+    x = synth.activations(m, k, workload=9, item=21)
+    planes, meta, _ = O.pack_rtn(w, 8, sg)
+    lo, hi = O.split_nibbles(planes)
+    coarse, ids, exact = O.screened_readout(x, hi, lo, meta, sg, n, k, cand)
+    full = O.linear_rtn(x, planes, meta, sg, 8, n, k)
+    for t in range(m):
+        assert np.allclose(exact[t], full[t, ids[t]], rtol=0, atol=1e-12 * np.abs(full).max())
+        assert int(np.argmax(full[t])) in ids[t].tolist()
+    s8, _ = O.unpack_meta(meta, n, k)
+    xr = np.abs(O.rotate(x.astype(np.float64), sg)).reshape(m, k // 128, 128).sum(-1)   # [M][G]
+    bound = 7.5 * xr @ s8.astype(np.float64).T                                          # [M][N]
+    assert np.all(np.abs(full - coarse) <= bound * (1 + 1e-12))
