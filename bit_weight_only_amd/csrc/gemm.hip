@@ -345,6 +345,27 @@ GemmPlan gemm_rtn_plan(int M, int K, int N, int bits) {
   }
   // slices short enough for the kernel to stage their scale/zero words in LDS
   while ((G + p.S - 1) / p.S > gemm_rtn_meta_max_groups(p.nb)) p.S *= 2;
+  // Grids of up to two workgroups per compute unit leave one wavefront per
+  // SIMD, which then waits alone on its loads and barriers: there two wave
+  // sets per workgroup (alternate groups of the slice) run on half as many
+  // workgroups, from two row blocks per wave (tiles of 64 tokens) or half the
+  // split (fewer tokens), whichever the sweep favoured. Larger grids already
+  // hold two workgroups per compute unit, and the 512-thread form, with twice
+  // the activation ring in LDS, measured slower there.
+  if (static_cast<long>(p.n_tiles) * p.m_tiles * p.S <= 512 && p.nb <= 2) {
+    GemmPlan q = p;
+    q.kw = 2;
+    if (p.mt == 4 && p.nb == 1) {
+      q.nb = 2;
+      q.n_tiles = (N + 127) / 128;
+    } else if (p.S >= 2) {
+      q.S = p.S / 2;
+    } else if (p.nb == 1) {
+      q.nb = 2;
+      q.n_tiles = (N + 127) / 128;
+    }
+    if ((G + q.S - 1) / q.S <= gemm_rtn_meta_max_groups(q.nb)) p = q;
+  }
   return p;
 }
 

@@ -16,10 +16,14 @@
 // is one MFMA per 16 groups at the end of the slice: A holds (T_g/16 high,
 // T_g/16 low) fp16 pairs per (token, group), B the pairs (-16 s z, -16 s z).
 //
-// Tiling: a workgroup of 4 wavefronts owns 64 NB output rows and 16 MT tokens;
-// wave w owns NB blocks of 16 rows, so each A fragment read from LDS feeds NB
-// MFMAs. The workgroup's K range is one of S slices of the 128-groups (split-K
-// when the tile grid alone leaves the chip idle). Per group:
+// Tiling: a workgroup of 4 KW wavefronts owns 64 NB output rows and 16 MT
+// tokens; row wave w (= wave mod 4) owns NB blocks of 16 rows, so each A
+// fragment read from LDS feeds NB MFMAs. The workgroup's K range is one of S
+// slices of the 128-groups (split-K when the tile grid alone leaves the chip
+// idle). With KW = 2 the two wave sets take alternate groups of the slice, so
+// each SIMD holds two wavefronts that hide each other's waits, and their
+// accumulators are added in LDS at the end (set 0 + set 1: a fixed order).
+// Per group:
 //  * the token tile's rotated activations (folded slot order: u32 slot c of a
 //    32-chunk = (x[c], x[c + 16])) are copied global -> LDS asynchronously into
 //    a ring of three slots, two groups ahead, one barrier per group;
@@ -180,21 +184,25 @@ __device__ __forceinline__ void decode_biased(const uint32_t *w, uint32_t h[16])
 }
 
 // One workgroup's tile: the mainloop shared by the dense and the grouped GEMM.
-template <int BITS, int NB, int MT, bool GROUPED>
+template <int BITS, int NB, int MT, int KW, bool GROUPED>
 __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 *planes, const uint32_t *meta,
                                               const TokenTile tt, uint4 *const *xs, uint32_t *msm) {
+  static_assert(KW == 1 || (KW == 2 && NB <= 2), "wave sets");
+  constexpr int kAll = kThreads * KW;    // threads of the workgroup
+  constexpr int kSlot = 16 * MT * 16;    // 16-byte vectors of one group's activations in a ring slot
   constexpr int U = NB * BITS;           // 16-byte plane vectors of a wave's rows per group
   constexpr int T = (U + 3) / 4;         // of them per lane
   constexpr int D = kRing - 1;           // groups in flight
   constexpr int CA = MT;                 // activation copies per wave per group (16 MT rows x 256 B)
   constexpr int kLoads = CA + T;         // vector-memory operations per wave per group
   constexpr int kRowsWG = kWaves * 16 * NB;
-  constexpr int kMetaIters = (kRowsWG * meta_vectors(meta_max_groups(NB)) + kThreads - 1) / kThreads;
+  constexpr int kMetaIters = (kRowsWG * meta_vectors(meta_max_groups(NB)) + kAll - 1) / kAll;
   constexpr int C = gemm_num_classes<BITS>();
   // msm: [kRowsWG][a.MS] (s, z) of group gb0 + c at column c; xs: the ring slots
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = (threadIdx.x >> 6) & (kWaves - 1);   // row wave
+  const int kh = static_cast<int>(threadIdx.x) / kThreads;   // wave set: groups g0 + kh, g0 + kh + KW, ...
   const int j = lane & 15, kq = lane >> 4;
   const int G = a.K / kGroup;
   const int split = blockIdx.x;
@@ -235,7 +243,7 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
   uint4 mst[kMetaIters];
 #pragma unroll
   for (int it = 0; it < kMetaIters; ++it) {
-    const int i = static_cast<int>(threadIdx.x) + it * kThreads;
+    const int i = static_cast<int>(threadIdx.x) + it * kAll;
     const int r = i / nq, v = i - r * nq, row = blockIdx.y * kRowsWG + r;
     const uint32_t off = (r < kRowsWG && row < a.N) ? (static_cast<uint32_t>(row) * G + gb0) * 4 + v * 16 : kOutOfRange;
     mst[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(mrs, off, 0, 0));
@@ -260,12 +268,15 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // loads of group g into ring slot q (past the slice: the activation copies
-  // repeat the slice's last group, the code and meta loads return zeros)
-  auto issue = [&](int q, int g) {
+  // loads of step st (this wave set's group g0 + KW st + kh) into ring slot q
+  // (past the slice: the activation copies repeat the slice's last group, the
+  // code loads return zeros)
+  auto issue = [&](int q, int st) {
+    const int g = g0 + KW * st + kh;
     const int gc = min(g, g1 - 1);
 #pragma unroll
-    for (int i = 0; i < CA; ++i) copy16_to_lds(asrc[i] + static_cast<size_t>(gc) * 16, xs[q] + 64 * (CA * wave + i));
+    for (int i = 0; i < CA; ++i)
+      copy16_to_lds(asrc[i] + static_cast<size_t>(gc) * 16, xs[q] + kh * kSlot + 64 * (CA * wave + i));
     const uint32_t past = g < g1 ? 0u : kOutOfRange;
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -277,7 +288,7 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
 
   auto contract = [&](int q, int g) {
     // the group's A fragments first: their LDS latency overlaps the decode
-    const uint4 *slot = xs[q];
+    const uint4 *slot = xs[q] + kh * kSlot;
     half8_t av[4][MT];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -325,11 +336,11 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
   };
 
 #pragma unroll
-  for (int q = 0; q < D; ++q) issue(q, g0 + q);
+  for (int q = 0; q < D; ++q) issue(q, q);
   // the staged words into LDS (visible after the loop's first barrier)
 #pragma unroll
   for (int it = 0; it < kMetaIters; ++it) {
-    const int i = static_cast<int>(threadIdx.x) + it * kThreads;
+    const int i = static_cast<int>(threadIdx.x) + it * kAll;
     const int r = i / nq, v = i - r * nq;
     if (r < kRowsWG) {
       uint32_t *dst = msm + r * a.MS + 4 * v;
@@ -339,22 +350,24 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
       dst[3] = mst[it].w;
     }
   }
-  for (int g = g0; g < g1; g += kRing) {
+  const int nst = (g1 - g0 + KW - 1) / KW;   // steps (the same count for every wave set)
+  for (int st = 0; st < nst; st += kRing) {
 #pragma unroll
     for (int q = 0; q < kRing; ++q) {
-      // group g + q: its loads are the oldest kLoads of this wave's D groups in
+      // step st + q: its loads are the oldest kLoads of this wave's D steps in
       // flight; after the barrier every wave's copies are in LDS and every wave
       // is done reading the slot refilled next
       wait_vm_lds<(D - 1) * kLoads>();
       __builtin_amdgcn_s_barrier();
-      issue((q + D) % kRing, g + q + D);
-      if (g + q < g1) contract(q, g + q);
+      issue((q + D) % kRing, st + q + D);
+      const int g = g0 + KW * (st + q) + kh;
+      if (g < g1) contract(q, g);
     }
   }
 
   // zero-point term of the slice: K = (group, high/low) over 16 groups per MFMA;
-  // lane (j, kq) covers groups 16 c + 4 kq .. + 3
-  for (int c16 = g0 / 16; c16 <= (g1 - 1) / 16; ++c16) {
+  // lane (j, kq) covers groups 16 c + 4 kq .. + 3 (the wave sets alternate)
+  for (int c16 = g0 / 16 + kh; c16 <= (g1 - 1) / 16; c16 += KW) {
     half8_t za[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -377,8 +390,34 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
     }
   }
   wait_vm_lds<0>();   // no copy into LDS may outlive the workgroup
+  if constexpr (KW > 1) {
+    // set 1 hands its accumulators to set 0 through the first ring slot
+    // (NB MT 4 floats per thread: NB MT 4 KB per wave set)
+    static_assert(NB * MT * 4 * kThreads * 4 <= kSlot * 16 * KW, "reduction buffer");
+    float *red = reinterpret_cast<float *>(xs[0]) + threadIdx.x % kThreads;
+    __syncthreads();   // every wave is done with the ring
+    if (kh == 1) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((nb * MT + mt) * 4 + r) * kThreads] = acc[nb][mt][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nb][mt][r] += red[((nb * MT + mt) * 4 + r) * kThreads];
+    }
+  }
+  const bool lead = kh == 0;   // the wave set that holds the sums
 
   if constexpr (GROUPED) {
+    if (!lead) return;
     // fp32 results by output row of each list entry (no split-K here)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -402,12 +441,14 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
     // publish this slice's partial tile; the last slice to arrive sums them all
     constexpr int kTileFloats = NB * MT * 4 * kThreads;
     float *mine = a.part + (static_cast<size_t>(tile_id) * a.S + split) * kTileFloats + threadIdx.x;
+    if (lead) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) store_coherent(mine + ((nb * MT + mt) * 4 + r) * kThreads, acc[nb][mt][r]);
+          for (int r = 0; r < 4; ++r) store_coherent(mine + ((nb * MT + mt) * 4 + r) * kThreads, acc[nb][mt][r]);
+    }
     wait_vm_lds<0>();   // the stores above have completed
     __syncthreads();
     __shared__ uint32_t last;
@@ -417,7 +458,7 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
                  ? 1u
                  : 0u;
     __syncthreads();
-    if (!last) return;
+    if (!last || !lead) return;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -433,6 +474,7 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
     }
   }
 
+  if (!lead) return;
   // D layout: lane holds tokens 4 kq + r (r = 0..3) of token tile mt, row j of block nb
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -452,23 +494,23 @@ __device__ __forceinline__ void gemm_rtn_body(const RtnGemmArgs &a, const uint4 
 
 // The ring slots are separate LDS objects so the compiler can tell that a read
 // of one slot does not depend on the copies in flight into the others.
-#define LBQ_RING_SLOTS(MT)                                                                              \
-  __shared__ __attribute__((aligned(16))) uint4 xs0[16 * (MT) * 16];                                    \
-  __shared__ __attribute__((aligned(16))) uint4 xs1[16 * (MT) * 16];                                    \
-  __shared__ __attribute__((aligned(16))) uint4 xs2[kRing > 2 ? 16 * (MT) * 16 : 1];                   \
-  __shared__ __attribute__((aligned(16))) uint4 xs3[kRing > 3 ? 16 * (MT) * 16 : 1];                   \
-  __shared__ __attribute__((aligned(16))) uint4 xs4[kRing > 4 ? 16 * (MT) * 16 : 1];                   \
-  __shared__ __attribute__((aligned(16))) uint4 xs5[kRing > 5 ? 16 * (MT) * 16 : 1];                   \
-  __shared__ __attribute__((aligned(16))) uint4 xs6[kRing > 6 ? 16 * (MT) * 16 : 1];                   \
-  __shared__ __attribute__((aligned(16))) uint4 xs7[kRing > 7 ? 16 * (MT) * 16 : 1];                   \
+#define LBQ_RING_SLOTS(MT, KW)                                                                          \
+  __shared__ __attribute__((aligned(16))) uint4 xs0[(KW) * 16 * (MT) * 16];                             \
+  __shared__ __attribute__((aligned(16))) uint4 xs1[(KW) * 16 * (MT) * 16];                             \
+  __shared__ __attribute__((aligned(16))) uint4 xs2[kRing > 2 ? (KW) * 16 * (MT) * 16 : 1];            \
+  __shared__ __attribute__((aligned(16))) uint4 xs3[kRing > 3 ? (KW) * 16 * (MT) * 16 : 1];            \
+  __shared__ __attribute__((aligned(16))) uint4 xs4[kRing > 4 ? (KW) * 16 * (MT) * 16 : 1];            \
+  __shared__ __attribute__((aligned(16))) uint4 xs5[kRing > 5 ? (KW) * 16 * (MT) * 16 : 1];            \
+  __shared__ __attribute__((aligned(16))) uint4 xs6[kRing > 6 ? (KW) * 16 * (MT) * 16 : 1];            \
+  __shared__ __attribute__((aligned(16))) uint4 xs7[kRing > 7 ? (KW) * 16 * (MT) * 16 : 1];            \
   uint4 *const xs[8] = {xs0, xs1, xs2, xs3, xs4, xs5, xs6, xs7};                                        \
   extern __shared__ uint32_t msm[];
 
-template <int BITS, int NB, int MT>
-__global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
-  LBQ_RING_SLOTS(MT)
-  gemm_rtn_body<BITS, NB, MT, false>(a, a.planes, a.meta, TokenTile{static_cast<int>(blockIdx.z) * 16 * MT, 0, 0}, xs,
-                                     msm);
+template <int BITS, int NB, int MT, int KW>
+__global__ void __launch_bounds__(kThreads * KW) gemm_rtn_kernel(RtnGemmArgs a) {
+  LBQ_RING_SLOTS(MT, KW)
+  gemm_rtn_body<BITS, NB, MT, KW, false>(a, a.planes, a.meta, TokenTile{static_cast<int>(blockIdx.z) * 16 * MT, 0, 0},
+                                         xs, msm);
 }
 
 // Grouped GEMM over routed experts: workgroup (., y, z) takes row tile y of
@@ -476,47 +518,49 @@ __global__ void __launch_bounds__(kThreads) gemm_rtn_kernel(RtnGemmArgs a) {
 template <int NB, int MT>
 __global__ void __launch_bounds__(kThreads) gemm_rtn_grouped_kernel(RtnGemmArgs a) {
   if (static_cast<int>(blockIdx.z) >= *a.n_tiles) return;
-  LBQ_RING_SLOTS(MT)
+  LBQ_RING_SLOTS(MT, 1)
   const int4 d = a.tiles[blockIdx.z];   // (e, i0, cnt, bits)
   const uint4 *pl = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(a.planes) + a.plane_off[d.x]);
   const uint32_t *mt = reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(a.meta) + a.meta_off[d.x]);
   const TokenTile tt{0, d.y, d.z};
-  if (d.w == 2) gemm_rtn_body<2, NB, MT, true>(a, pl, mt, tt, xs, msm);
-  else if (d.w == 3) gemm_rtn_body<3, NB, MT, true>(a, pl, mt, tt, xs, msm);
-  else gemm_rtn_body<4, NB, MT, true>(a, pl, mt, tt, xs, msm);
+  if (d.w == 2) gemm_rtn_body<2, NB, MT, 1, true>(a, pl, mt, tt, xs, msm);
+  else if (d.w == 3) gemm_rtn_body<3, NB, MT, 1, true>(a, pl, mt, tt, xs, msm);
+  else gemm_rtn_body<4, NB, MT, 1, true>(a, pl, mt, tt, xs, msm);
 }
 #undef LBQ_RING_SLOTS
 
-template <int BITS, int NB, int MT>
+template <int BITS, int NB, int MT, int KW>
 hipError_t launch_rtn(dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
   const size_t lds = static_cast<size_t>(kWaves * 16 * NB) * a.MS * 4;
-  const size_t ring = static_cast<size_t>(kRing) * 16 * MT * 16 * 16;   // the static activation slots
-  auto kern = gemm_rtn_kernel<BITS, NB, MT>;
+  const size_t ring = static_cast<size_t>(kRing) * KW * 16 * MT * 16 * 16;   // the static activation slots
+  auto kern = gemm_rtn_kernel<BITS, NB, MT, KW>;
   if (ring + lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads * KW), lds, s, a);
   return hipGetLastError();
+}
+
+template <int BITS, int NB>
+hipError_t launch_rtn_mt(const GemmPlan &p, dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
+  if (NB <= 2 && p.kw == 2) {
+    constexpr int KW = NB <= 2 ? 2 : 1;
+    if (p.mt == 1) return launch_rtn<BITS, NB, 1, KW>(grid, a, s);
+    if (p.mt == 2) return launch_rtn<BITS, NB, 2, KW>(grid, a, s);
+    return launch_rtn<BITS, NB, 4, KW>(grid, a, s);
+  }
+  if (p.mt == 1) return launch_rtn<BITS, NB, 1, 1>(grid, a, s);
+  if (p.mt == 2) return launch_rtn<BITS, NB, 2, 1>(grid, a, s);
+  return launch_rtn<BITS, NB, 4, 1>(grid, a, s);
 }
 
 template <int BITS>
 hipError_t launch_rtn_bits(const GemmPlan &p, dim3 grid, const RtnGemmArgs &a, hipStream_t s) {
-  if (BITS != 8 && p.nb == 4) {
-    constexpr int NB4 = BITS == 8 ? 2 : 4;   // (8-bit codes: no four-block plans)
-    if (p.mt == 1) return launch_rtn<BITS, NB4, 1>(grid, a, s);
-    if (p.mt == 2) return launch_rtn<BITS, NB4, 2>(grid, a, s);
-    return launch_rtn<BITS, NB4, 4>(grid, a, s);
-  }
-  if (p.nb == 2) {
-    if (p.mt == 1) return launch_rtn<BITS, 2, 1>(grid, a, s);
-    if (p.mt == 2) return launch_rtn<BITS, 2, 2>(grid, a, s);
-    return launch_rtn<BITS, 2, 4>(grid, a, s);
-  }
-  if (p.mt == 1) return launch_rtn<BITS, 1, 1>(grid, a, s);
-  if (p.mt == 2) return launch_rtn<BITS, 1, 2>(grid, a, s);
-  return launch_rtn<BITS, 1, 4>(grid, a, s);
+  if (BITS != 8 && p.nb == 4) return launch_rtn_mt<BITS, BITS == 8 ? 2 : 4>(p, grid, a, s);   // (8-bit: no four-block plans)
+  if (p.nb == 2) return launch_rtn_mt<BITS, 2>(p, grid, a, s);
+  return launch_rtn_mt<BITS, 1>(p, grid, a, s);
 }
 
 }  // namespace
@@ -576,7 +620,8 @@ bool gemm_rtn_supported(int K, int N, int bits) {
 hipError_t launch_gemm_rtn(const GemmPlan &p, int bits, const void *planes, const void *meta, const uint16_t *xf,
                            const uint32_t *tz, uint16_t *y, int M, int K, int N, void *scratch, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if ((p.nb != 1 && p.nb != 2 && p.nb != 4) || (p.mt != 1 && p.mt != 2 && p.mt != 4) || p.S < 1)
+  if ((p.nb != 1 && p.nb != 2 && p.nb != 4) || (p.mt != 1 && p.mt != 2 && p.mt != 4) || p.S < 1 ||
+      (p.kw != 1 && p.kw != 2) || (p.kw == 2 && p.nb == 4))
     return hipErrorInvalidValue;
   if ((bits < 2 || bits > 4) && bits != 8) return hipErrorInvalidValue;
   if (!gemm_rtn_supported(K, N, bits) || (bits == 8 && p.nb > 2)) return hipErrorInvalidValue;

@@ -10,6 +10,16 @@
 namespace lbq {
 
 hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, hipStream_t s);
+
+// Screened readout (readout.hip): the survivors' selection by coarse logit
+// (keys: readout_key_bytes of scratch; *final_keys receives the [M][cand]
+// sorted survivors inside it) and their exact logits from the nibble planes.
+size_t readout_key_bytes(int M, int N, int cand);
+hipError_t launch_readout_select(const uint16_t *coarse, int M, int N, int cand, uint64_t *keys,
+                                 const uint64_t **final_keys, hipStream_t s);
+hipError_t launch_readout_refine(const uint64_t *keys, const void *hi, const void *lo, const void *meta,
+                                 const uint16_t *xr, int M, int K, int N, int cand, int32_t *ids, float *logits,
+                                 hipStream_t s);
 // Rotation into the folded slot order (u32 slot c of each 32-chunk holds
 // (x'[c], x'[c+16])); with tz non-null also the RTN GEMM's per-(token, group)
 // sums tz[m * gemm_tz_stride(K) + g] = (T/16 high, T/16 low) fp16, zero-padded;
@@ -61,6 +71,7 @@ hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, con
 // GEMM starts.
 struct GemmPlan {
   int nb, mt, S, n_tiles, m_tiles;
+  int kw = 1;   // RTN GEMM: wave sets per workgroup (2: alternate groups, 512 threads)
 };
 GemmPlan gemm_plan(int M, int K, int N);
 GemmPlan gemm_rtn_plan(int M, int K, int N, int bits);
