@@ -29,7 +29,9 @@ extra: every other part of the hot path, each against its own roofline: the
 single 4096x4096 linear, the stack at M = 4 and 16, the 5120/17408 FFN pair at
 M = 1, 8, 64, 256 (the TFLOP/s at M = 64 is the metric's second half), the
 product-VQ 4096->14336 linear at M = 1, 16, 64, the 256-expert MoE block at
-M = 32, the router and the rotation alone.
+M = 32 (and its prefill at 256 and 2048 tokens), the router and the rotation
+alone, and the screened readout of an 8-bit 2048 -> 131072 vocabulary weight
+against its plain 8-bit readout.
 
 Every extra cycles over device copies of its weights totalling at least
 1 GiB (four times the 256 MB last-level cache), so repeats stream from HBM, and
@@ -615,6 +617,62 @@ def extra_pvq(torch, L, steps, Ms=None):
     return res
 
 
+def extra_readout(torch, L, steps, Ms=None):
+    """Screened readout over the nibble-split planes of an 8-bit vocabulary
+    weight against the plain 8-bit readout (lbq_linear_forward at 8 bits) of
+    the same weight; each call on its own device copy (pool of 1 GiB or more).
+    Bytes: the screen reads the high-nibble planes and their scale/zero words
+    of every row (half the 8-bit planes), plus both nibble planes of the
+    survivors; the plain readout reads all 8-bit planes and meta."""
+    cfg = synth.READOUT
+    K, N, cand = cfg["K"], cfg["N"], cfg["cand"]
+    dev = torch.device("cuda:0")
+    w = synth.weights(N, K, workload=synth.W_READOUT)
+    s = synth.signs(K, workload=synth.W_READOUT)
+    planes, meta = L.pack(w, 8, s)
+    del w
+    hi, lo, hm = L.split_nibbles(planes, meta, K, N)
+    s_dev = torch.from_numpy(s).to(dev)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1)).to(dev)
+
+    n_copies = copies_for(hi.nbytes + lo.nbytes + hm.nbytes + meta.nbytes)
+    ros = [L.PackedReadout(K, N, up(hi), up(lo), up(hm), up(meta), s_dev) for _ in range(n_copies)]
+    screen_bytes = hi.nbytes + hm.nbytes
+    lin8 = Linears(L, torch, K, N, 8, L.FMT_RTN_PLANES, planes, meta, s, None,
+                   copies_for(planes.nbytes + meta.nbytes))
+    del hi, lo, hm, planes
+    lib = L.lib()
+    res = {}
+    for M in (Ms or cfg["M"]):
+        x = torch.from_numpy(synth.activations(M, K, workload=synth.W_READOUT, item=M)).to(dev)
+        coarse = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ids = torch.empty((M, cand), dtype=torch.int32, device=dev)
+        lg = torch.empty((M, cand), dtype=torch.float32, device=dev)
+        ws = torch.empty(ros[0].workspace_bytes(M, cand), dtype=torch.uint8, device=dev)
+
+        def fn(sp):
+            for r in ros:
+                check(lib.lbq_readout_screened(ctypes.byref(r.struct), ctypes.c_void_p(x.data_ptr()), M, cand,
+                                               ctypes.c_void_p(coarse.data_ptr()), ctypes.c_void_p(ids.data_ptr()),
+                                               ctypes.c_void_p(lg.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                               ws.numel(), sp), "lbq_readout_screened")
+        per_step = []
+        t = time_graph(torch, fn, steps, 2, per_step) / steps / len(ros)
+        surv = M * cand * (K // 128) * 128   # both nibble planes of every survivor
+        full = measure_linears(torch, L, lin8, M, steps, x=x)
+        res[f"M{M}"] = {"M": M, "cand": cand, "us_per_call": round(t * 1e6, 3),
+                        "us_per_call_stats": stats(per_step, 1e6 / len(ros)),
+                        "screen_bytes": screen_bytes, "GBps": round((screen_bytes + surv) / t / 1e9, 1),
+                        "frac": round((screen_bytes + surv) / t / 1e9 / HBM_PEAK_GBS, 4),
+                        "full_8bit_us": full["us_per_call"], "speedup_vs_full_8bit": round(full["us_per_call"] / (t * 1e6), 3)}
+        del coarse, ids, lg, ws
+    del ros, lin8
+    torch.cuda.empty_cache()
+    return res
+
+
 def extra_moe(torch, L, steps, extras=True, M=None):
     cfg = synth.MOE_BLOCK
     E, H, F, k = cfg["E"], cfg["hidden"], cfg["ffn"], cfg["top_k"]
@@ -994,7 +1052,7 @@ def planes_meta_bytes(k, n, bits):
 # ---------------------------------------------------------------- main
 
 CASES = ("stack1", "stack4", "stack16", "single", "ffn1", "ffn8", "ffn64", "ffn256", "pvq1", "pvq16", "pvq64", "moe",
-         "moe256", "moe2048")
+         "moe256", "moe2048", "readout1", "readout4")
 
 
 def run_case(torch, L, case, steps):
@@ -1008,6 +1066,8 @@ def run_case(torch, L, case, steps):
         r = extra_ffn(torch, L, steps, Ms=(int(case[3:]),))
     elif case.startswith("pvq"):
         r = extra_pvq(torch, L, steps, Ms=(int(case[3:]),))
+    elif case.startswith("readout"):
+        r = extra_readout(torch, L, steps, Ms=(int(case[7:]),))
     else:
         r = extra_moe(torch, L, steps, extras=False, M=int(case[3:]) if len(case) > 3 else None)
     print(json.dumps({"case": case, "result": r}), flush=True)
@@ -1142,6 +1202,8 @@ def main():
         for M in (256, 2048):
             log(f"[bench] extra: MoE block, {M} tokens (prefill)")
             extra[f"moe_block_M{M}"] = extra_moe(torch, L, max(3, steps // 2), extras=False, M=M)
+        log("[bench] extra: screened readout 2048 -> 131072 (8-bit, nibble-split)")
+        extra["readout"] = extra_readout(torch, L, steps)
         m64 = extra["ffn_pair"]["M64"]
         extra["TFLOPs_at_M64"] = {"value": m64["TFLOPs"], "frac_of_mfma_peak": round(m64["TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
                                   "workload": "FFN pair 5120->17408 (2-bit) + 17408->5120 (3-bit), M=64"}

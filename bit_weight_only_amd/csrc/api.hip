@@ -360,6 +360,15 @@ lbq_status check_moe(const lbq_moe *m, int M) {
 
 extern "C" {
 
+lbq_status lbq_split_nibbles(const void *planes8, const void *meta8, int32_t K, int32_t N, void *hi_planes,
+                             void *lo_planes, void *hi_meta) {
+  if (!planes8 || !meta8 || !hi_planes || !lo_planes || !hi_meta) return LBQ_ERR_NULL;
+  if (K <= 0 || K % 128 != 0 || N <= 0) return LBQ_ERR_SHAPE;
+  return split_nibbles(static_cast<const uint32_t *>(planes8), static_cast<const uint16_t *>(meta8), K, N,
+                       static_cast<uint32_t *>(hi_planes), static_cast<uint32_t *>(lo_planes),
+                       static_cast<uint16_t *>(hi_meta));
+}
+
 lbq_status lbq_moe_workspace(const lbq_moe *m, int32_t M, size_t *bytes) {
   if (!bytes) return LBQ_ERR_NULL;
   lbq_status st = check_moe(m, M);
@@ -439,6 +448,80 @@ lbq_status lbq_moe_route(const float *logits, int32_t M, int32_t E, int32_t top_
   if (!ids || !weights || !counts || !offsets || !perm || (M > 0 && !logits)) return LBQ_ERR_NULL;
   return hip_status(launch_moe_route(logits, M, E, top_k, ids, weights, counts, offsets, perm,
                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- screened readout
+
+namespace {
+
+lbq_status check_readout(const lbq_readout *r, int M, int cand) {
+  if (!r || !r->hi_planes || !r->lo_planes || !r->hi_meta || !r->meta || !r->signs) return LBQ_ERR_NULL;
+  if (r->K <= 0 || r->K % 128 != 0 || r->N <= 0) return LBQ_ERR_SHAPE;
+  if (M < 0 || M > 65535 || cand < 1 || cand > 64) return LBQ_ERR_SHAPE;
+  if (!aligned16(r->hi_planes) || !aligned16(r->lo_planes) || !aligned16(r->hi_meta) || !aligned16(r->meta))
+    return LBQ_ERR_ALIGN;
+  return LBQ_OK;
+}
+
+// the high nibbles as a 4-bit weight of the library's own format
+lbq_weight readout_hi_weight(const lbq_readout *r) {
+  lbq_weight w{};
+  w.K = r->K;
+  w.N = r->N;
+  w.bits = 4;
+  w.format = LBQ_FMT_RTN_PLANES;
+  w.planes = r->hi_planes;
+  w.meta = r->hi_meta;
+  w.codebook = nullptr;
+  w.signs = r->signs;
+  return w;
+}
+
+// workspace: the coarse linear's own workspace, the fp16 rotated activations
+// of the exact step, the survivors' keys
+size_t readout_ws_bytes(const lbq_readout *r, int M, int cand) {
+  const lbq_weight w = readout_hi_weight(r);
+  return round_up(linear_ws_bytes(&w, M), kAlign) + round_up(static_cast<size_t>(M) * r->K * 2, kAlign) +
+         readout_key_bytes(M, r->N, cand);
+}
+
+}  // namespace
+
+extern "C" {
+
+lbq_status lbq_readout_workspace(const lbq_readout *r, int32_t M, int32_t cand, size_t *bytes) {
+  if (!bytes) return LBQ_ERR_NULL;
+  const lbq_status st = check_readout(r, M, cand);
+  if (st != LBQ_OK) return st;
+  *bytes = readout_ws_bytes(r, M, cand);
+  return LBQ_OK;
+}
+
+lbq_status lbq_readout_screened(const lbq_readout *r, const uint16_t *x, int32_t M, int32_t cand, uint16_t *coarse,
+                                int32_t *ids, float *logits, void *ws, size_t ws_bytes, void *stream) {
+  lbq_status st = check_readout(r, M, cand);
+  if (st != LBQ_OK) return st;
+  if (M == 0) return LBQ_OK;
+  if (!x || !coarse || !ids || !logits || !ws) return LBQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(coarse) || !aligned16(ws)) return LBQ_ERR_ALIGN;
+  if (ws_bytes < readout_ws_bytes(r, M, cand)) return LBQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lbq_weight w = readout_hi_weight(r);
+  const size_t lin = round_up(linear_ws_bytes(&w, M), kAlign);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  uint16_t *xr = reinterpret_cast<uint16_t *>(base + lin);
+  uint64_t *keys = reinterpret_cast<uint64_t *>(base + lin + round_up(static_cast<size_t>(M) * r->K * 2, kAlign));
+  // 1. coarse logits of every row from the high nibbles
+  st = forward_impl(&w, x, M, coarse, ws, lin, LBQ_PATH_AUTO, stream, nullptr, nullptr);
+  if (st != LBQ_OK) return st;
+  // 2. the survivors per token, 3. their exact logits
+  const uint64_t *fin = nullptr;
+  if (launch_rotate(x, M, r->K, r->signs, xr, s) != hipSuccess) return LBQ_ERR_HIP;
+  if (launch_readout_select(coarse, M, r->N, cand, keys, &fin, s) != hipSuccess) return LBQ_ERR_HIP;
+  return hip_status(launch_readout_refine(fin, r->hi_planes, r->lo_planes, r->meta, xr, M, r->K, r->N, cand, ids,
+                                          logits, s));
 }
 
 }  // extern "C"

@@ -265,4 +265,21 @@ lbq_status pack_pvq(const float *W, int K, int N, const int8_t *signs, const uin
   return static_cast<lbq_status>(err.load());
 }
 
+lbq_status split_nibbles(const uint32_t *planes8, const uint16_t *meta8, int K, int N, uint32_t *hi, uint32_t *lo,
+                         uint16_t *hi_meta) {
+  const size_t groups = static_cast<size_t>(N) * (K / 128);
+  for (size_t i = 0; i < groups; ++i) {
+    // planes 0..3 of a group are the low nibble's bits, planes 4..7 the high one's
+    std::memcpy(lo + i * 16, planes8 + i * 32, 64);
+    std::memcpy(hi + i * 16, planes8 + i * 32 + 16, 64);
+    const double s = f16_to_f64(meta8[2 * i]), z = f16_to_f64(meta8[2 * i + 1]);
+    const double sh = 16.0 * s, zh = (z - 7.5) / 16.0;
+    const uint16_t a = f64_to_f16_rne(sh), b = f64_to_f16_rne(zh);
+    if (!std::isfinite(sh) || !std::isfinite(zh) || f16_to_f64(a) != sh || f16_to_f64(b) != zh) return LBQ_ERR_RANGE;
+    hi_meta[2 * i] = a;
+    hi_meta[2 * i + 1] = b;
+  }
+  return LBQ_OK;
+}
+
 }  // namespace lbq

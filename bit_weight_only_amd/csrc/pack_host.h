@@ -36,4 +36,9 @@ lbq_status gptq_factor(const double *H, int K, const int8_t *signs, double damp,
 lbq_status pack_gptq(const float *W, int K, int N, int bits, const int8_t *signs, const double *U,
                      uint32_t *planes, uint16_t *meta);
 
+// Nibble split of 8-bit planes and meta: planes 4..7 / 0..3 of every group to
+// hi / lo ([N][G][4][4] u32 each), and the high nibbles' (16 s, (z - 7.5) / 16).
+lbq_status split_nibbles(const uint32_t *planes8, const uint16_t *meta8, int K, int N, uint32_t *hi, uint32_t *lo,
+                         uint16_t *hi_meta);
+
 }  // namespace lbq

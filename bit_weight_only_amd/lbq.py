@@ -31,7 +31,7 @@ EXPORTS = [
     "lbq_status_string", "lbq_packed_bytes", "lbq_pack", "lbq_linear_workspace", "lbq_linear_forward",
     "lbq_linear_forward_path", "lbq_linear_forward_timed", "lbq_moe_workspace", "lbq_moe_forward", "lbq_moe_route", "lbq_unpack_codes",
     "lbq_rotate", "lbq_linear_forward_noalloc", "lbq_stream_read", "lbq_gptq_factor",
-    "lbq_pack_gptq", "lbq_moe_forward_path",
+    "lbq_pack_gptq", "lbq_moe_forward_path", "lbq_split_nibbles", "lbq_readout_workspace", "lbq_readout_screened",
 ]
 
 
@@ -52,6 +52,12 @@ class Moe(ctypes.Structure):
                 ("bits", ctypes.c_void_p), ("gu_plane_off", ctypes.c_void_p), ("gu_meta_off", ctypes.c_void_p),
                 ("dn_plane_off", ctypes.c_void_p), ("dn_meta_off", ctypes.c_void_p), ("planes", ctypes.c_void_p),
                 ("meta", ctypes.c_void_p), ("signs_hidden", ctypes.c_void_p), ("signs_ffn", ctypes.c_void_p)]
+
+
+class Readout(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("hi_planes", ctypes.c_void_p),
+                ("lo_planes", ctypes.c_void_p), ("hi_meta", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+                ("signs", ctypes.c_void_p)]
 
 
 _lib = None
@@ -88,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.lbq_stream_read.argtypes = [c_vp, c_sz, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
         L.lbq_gptq_factor.argtypes = [c_vp, c_i32, c_vp, ctypes.c_double, c_vp]
         L.lbq_pack_gptq.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
+        L.lbq_split_nibbles.argtypes = [c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]
+        L.lbq_readout_workspace.argtypes = [ctypes.POINTER(Readout), c_i32, c_i32, p_sz]
+        L.lbq_readout_screened.argtypes = [ctypes.POINTER(Readout), c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                           c_vp]
         for name in EXPORTS:
             if name != "lbq_status_string":
                 getattr(L, name).restype = c_i32
@@ -238,6 +248,67 @@ def unpack_codes(w: PackedLinear, stream=None):
     codes = torch.empty(n, dtype=torch.uint8, device=w.planes.device)
     _check(lib().lbq_unpack_codes(ctypes.byref(w.struct), _ptr(codes), _stream(stream)), "lbq_unpack_codes")
     return codes.view(w.N, -1)
+
+
+# ------------------------------------------------------------------ screened readout
+
+def split_nibbles(planes8: np.ndarray, meta8: np.ndarray, K: int, N: int):
+    """lbq_split_nibbles on the host: (hi_planes, lo_planes, hi_meta) as uint8 arrays."""
+    planes8 = np.ascontiguousarray(planes8).view(np.uint8)
+    meta8 = np.ascontiguousarray(meta8).view(np.uint8)
+    G = K // 128
+    hi = np.empty(N * G * 64, np.uint8)
+    lo = np.empty(N * G * 64, np.uint8)
+    hm = np.empty(N * G * 4, np.uint8)
+    _check(lib().lbq_split_nibbles(planes8.ctypes.data, meta8.ctypes.data, K, N, hi.ctypes.data, lo.ctypes.data,
+                                   hm.ctypes.data), "lbq_split_nibbles")
+    return hi, lo, hm
+
+
+class PackedReadout:
+    """Device-resident nibble-split readout weight and its lbq_readout view."""
+
+    def __init__(self, K, N, hi_planes, lo_planes, hi_meta, meta, signs):
+        self.K, self.N = int(K), int(N)
+        self.hi_planes, self.lo_planes, self.hi_meta, self.meta, self.signs = hi_planes, lo_planes, hi_meta, meta, signs
+        self._r = Readout(self.K, self.N, hi_planes.data_ptr(), lo_planes.data_ptr(), hi_meta.data_ptr(),
+                          meta.data_ptr(), signs.data_ptr())
+
+    @classmethod
+    def from_host(cls, planes8: np.ndarray, meta8: np.ndarray, signs: np.ndarray, K: int, N: int, device="cuda"):
+        import torch
+
+        hi, lo, hm = split_nibbles(planes8, meta8, K, N)
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1)).to(device)
+
+        return cls(K, N, up(hi), up(lo), up(hm), up(meta8), torch.from_numpy(np.ascontiguousarray(signs, np.int8)).to(device))
+
+    @property
+    def struct(self) -> Readout:
+        return self._r
+
+    def workspace_bytes(self, M: int, cand: int) -> int:
+        b = ctypes.c_size_t()
+        _check(lib().lbq_readout_workspace(ctypes.byref(self._r), int(M), int(cand), ctypes.byref(b)),
+               "lbq_readout_workspace")
+        return b.value
+
+
+def readout_screened(r: PackedReadout, x, cand: int, ws=None, stream=None):
+    """lbq_readout_screened: (coarse fp16 [M][N], ids int32 [M][cand], exact logits fp32 [M][cand])."""
+    import torch
+
+    M = int(x.shape[0])
+    coarse = torch.empty((M, r.N), dtype=torch.float16, device=x.device)
+    ids = torch.empty((M, cand), dtype=torch.int32, device=x.device)
+    logits = torch.empty((M, cand), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(1, r.workspace_bytes(M, cand)), dtype=torch.uint8, device=x.device)
+    _check(lib().lbq_readout_screened(ctypes.byref(r.struct), _ptr(x), M, int(cand), _ptr(coarse), _ptr(ids),
+                                      _ptr(logits), _ptr(ws), ws.numel(), _stream(stream)), "lbq_readout_screened")
+    return coarse, ids, logits
 
 
 # ------------------------------------------------------------------ MoE

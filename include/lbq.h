@@ -12,7 +12,9 @@
  *     model card, "What this is");
  *   - the rotated weight W' = W R^T is held either as group-128 2/3/4-bit
  *     codes with an fp16 scale and zero per group (the LLaDA2.2-mini card's
- *     "Routed Experts" row: group-128 codes, mixed 2/3/4-bit per expert),
+ *     "Routed Experts" row: group-128 codes, mixed 2/3/4-bit per expert), or
+ *     8-bit codes of the same form (its "Non-Expert Path" and "Readout &
+ *     Embeddings" rows),
  *     packed as bit-planes in 32-bit words (Qwen3-8B 2-bit BPDQ model card,
  *     opening paragraph), or as product-VQ indices into a small codebook whose
  *     values sit on the fp8 e4m3 grid (Laguna-S-2.1 gridbook model card,
@@ -39,7 +41,7 @@
  *     is a valid no-op.
  *
  * Packed formats (byte-exact; little-endian):
- *   LBQ_FMT_RTN_PLANES, bits b in {2,3,4}, G = K/128:
+ *   LBQ_FMT_RTN_PLANES, bits b in {2,3,4,8}, G = K/128:
  *     planes: uint32 [N][G][b][4]. Bit j of word w of plane p holds bit p of
  *             code q[n][128 g + 32 w + j]. plane_bytes = N*K*b/8.
  *     meta:   [N][G] pairs of IEEE fp16 (scale s, zero z), s at the lower
@@ -66,10 +68,10 @@ typedef enum {
   LBQ_OK = 0,
   LBQ_ERR_NULL = -1,       /* a required pointer is NULL */
   LBQ_ERR_SHAPE = -2,      /* K not a positive multiple of 128, N <= 0, M < 0, top_k outside [1, E], ... */
-  LBQ_ERR_BITS = -3,       /* bits outside {2,3,4} (RTN) or != 2 (PVQ) */
+  LBQ_ERR_BITS = -3,       /* bits outside {2,3,4,8} (RTN) or != 2 (PVQ) */
   LBQ_ERR_ALIGN = -4,      /* a pointer that must be 16-byte aligned is not */
   LBQ_ERR_WORKSPACE = -5,  /* workspace smaller than the *_workspace query returned */
-  LBQ_ERR_RANGE = -6,      /* packing: non-finite weight or an RTN group scale of 128 or more */
+  LBQ_ERR_RANGE = -6,      /* packing: non-finite weight or an RTN group scale out of range */
   LBQ_ERR_HIP = -7,        /* a HIP launch reported an error */
   LBQ_ERR_FORMAT = -8      /* unknown format, or a format the entry point does not take */
 } lbq_status;
@@ -144,7 +146,7 @@ lbq_status lbq_packed_bytes(int32_t K, int32_t N, int32_t bits, int32_t format,
  *   W: host fp32 [N][K] row-major (PyTorch Linear layout, y = x W^T).
  *   signs: host int8 [K] of +-1.  codebook: host [256][4] e4m3 bytes (PVQ only).
  *   planes_out / meta_out: host buffers of lbq_packed_bytes' sizes.
- * RTN (bits 2/3/4): rotate each row per 128-block (signs, radix-2 butterflies,
+ * RTN (bits 2/3/4/8): rotate each row per 128-block (signs, radix-2 butterflies,
  * then c), then per group mn = min(0, min w'), mx = max(0, max w'),
  * s = fp16_rne((mx - mn) / (2^b - 1)) (0 -> 1), z = rint(-mn / s),
  * q = clamp(rint(w' / s) + z, 0, 2^b - 1), and scatter q into bit-planes.
@@ -152,8 +154,9 @@ lbq_status lbq_packed_bytes(int32_t K, int32_t N, int32_t bits, int32_t format,
  * 4-weight half the nearest codebook entry to w'/s_n (squared distance,
  * ties to the lower index).
  * Returns LBQ_ERR_RANGE for non-finite W, a PVQ scale that overflows fp16, or
- * an RTN scale s >= 128 (the MFMA GEMM's decode holds -64 s and -16 s z in
- * fp16; a group would need a weight range of 128 (2^b - 1) to reach it). */
+ * an RTN scale s >= 128 at 2/3/4 bits or s >= 16 at 8 bits (the MFMA GEMM's
+ * decode holds -64 s (-256 s at 8 bits) and -16 s z in fp16; a group would
+ * need a weight range of 128 (2^b - 1), or 16 * 255, to reach it). */
 lbq_status lbq_pack(const float *W, int32_t K, int32_t N, int32_t bits, int32_t format,
                     const int8_t *signs, const uint8_t *codebook,
                     void *planes_out, void *meta_out);
@@ -204,7 +207,9 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
  *   - M <= 4, K a multiple of 512, signs 16-byte aligned (PVQ: codebook 4-byte
  *     aligned): one launch, the matrix-core GEMV with the rotation in its
  *     prologue (nothing is written to ws);
- *   - other M <= 4: a rotation launch into ws, then the staged VALU GEMV;
+ *   - other M <= 4: a rotation launch into ws, then the staged VALU GEMV
+ *     (8-bit codes: the MFMA GEMM instead; a forced GEMV that the matrix-core
+ *     GEMV cannot take returns LBQ_ERR_SHAPE at 8 bits);
  *   - M >= 5: a rotation launch into ws (folded order, with the RTN
  *     zero-point sums), then the MFMA dequant-GEMM.
  * Accumulation is fp32; the GEMM rounds each decoded RTN weight s q to fp16
@@ -309,6 +314,53 @@ lbq_status lbq_unpack_codes(const lbq_weight *w, uint8_t *codes, void *stream);
  * fp16 out. x, out: device [M][K], 16-byte aligned; signs: device [K]. */
 lbq_status lbq_rotate(const uint16_t *x, int32_t M, int32_t K, const int8_t *signs,
                       uint16_t *out, void *stream);
+
+/* Nibble-split planes of an 8-bit weight, for the screened readout (host,
+ * offline). The readout keeps its 8-bit codes and the same codes split into
+ * high and low nibble planes (LLaDA2.2-mini card, property table, "Readout &
+ * Embeddings" row, and its file list). With q = 16 hi + lo:
+ *   planes8: host uint32 [N][K/128][8][4] and meta8: host fp16 pairs
+ *     [N][K/128][2] (s, z), as lbq_pack writes them at 8 bits;
+ *   hi_planes / lo_planes: host uint32 [N][K/128][4][4] out: planes 4..7 and
+ *     0..3, i.e. the 4-bit plane sets of hi and lo;
+ *   hi_meta: host fp16 pairs [N][K/128][2] out: (16 s, (z - 7.5) / 16), which
+ *     make hi_planes a 4-bit weight whose decode s (16 hi + 7.5 - z) takes
+ *     each high nibble at the middle of the 16 codes it spans.
+ * Errors: LBQ_ERR_NULL, LBQ_ERR_SHAPE (K not a positive multiple of 128, N <= 0),
+ * LBQ_ERR_RANGE (a scale or zero whose high-nibble form is not exact in fp16:
+ * outside what lbq_pack writes at 8 bits). */
+lbq_status lbq_split_nibbles(const void *planes8, const void *meta8, int32_t K, int32_t N,
+                             void *hi_planes, void *lo_planes, void *hi_meta);
+
+/* A readout weight in nibble-split form (device views, 16-byte aligned):
+ * hi_planes, lo_planes and hi_meta as lbq_split_nibbles writes them, meta the
+ * 8-bit (s, z) pairs, signs [K] +-1. */
+typedef struct {
+  int32_t K, N;
+  const void *hi_planes, *lo_planes, *hi_meta, *meta;
+  const int8_t *signs;
+} lbq_readout;
+
+/* Workspace bytes of lbq_readout_screened for M tokens and cand survivors
+ * (host query). Errors as lbq_readout_screened's argument checks. */
+lbq_status lbq_readout_workspace(const lbq_readout *r, int32_t M, int32_t cand, size_t *bytes);
+
+/* Screened readout (the LLaDA2.2-mini card's screened readout over the
+ * nibble-split planes of its 8-bit lm_head). Per token t:
+ *   1. coarse[t][n] (fp16, every row n) = x_t W_hi^T, W_hi the 4-bit weight
+ *      (hi_planes, hi_meta): half the bytes of the 8-bit weight, by the
+ *      lbq_linear_forward path for M tokens;
+ *   2. the cand rows with the largest coarse logits, larger first, ties to the
+ *      lower row (decided on the fp16 values of step 1);
+ *   3. their exact logits from both nibbles, q = 16 hi + lo with the 8-bit
+ *      (s, z), against the fp16-rotated x_t, fp32 accumulation.
+ *   x: fp16 [M][K]; coarse: fp16 [M][N] out; ids: int32 [M][cand] out (rows,
+ *   in step 2's order; -1 past the N-th when cand > N); logits: fp32
+ *   [M][cand] out (0 for -1 ids). 1 <= cand <= 64, M <= 65535.
+ * Errors as lbq_linear_forward, plus LBQ_ERR_SHAPE for cand or M out of range. */
+lbq_status lbq_readout_screened(const lbq_readout *r, const uint16_t *x, int32_t M, int32_t cand,
+                                uint16_t *coarse, int32_t *ids, float *logits, void *ws, size_t ws_bytes,
+                                void *stream);
 
 /* Measurement reference, not part of the layer: one launch of grid x block
  * threads (block a multiple of 64, at most 1024) that reads bytes (a multiple

@@ -129,6 +129,10 @@ DENSE_STACK_M = (1, 4, 16)
 MOE_BLOCK = dict(E=256, hidden=2048, ffn=1024, top_k=8, M=32)
 FFN_SWEEP = dict(K_gu=5120, N_gu=17408, bits_gu=2, bits_dn=3, M=(1, 8, 64, 256))
 PVQ_LINEAR = dict(K=4096, N=14336, M=(1, 16, 64))
+# 8-bit readout over a vocabulary: hidden 2048 as in the MoE block; the pages
+# give no vocabulary size, 131072 rows stands in for one
+READOUT = dict(K=2048, N=131072, M=(1, 4), cand=64)
 
 # Workload numbers used as the first seed component.
 W_SINGLE, W_STACK, W_MOE, W_FFN, W_PVQ = 0, 1, 2, 3, 4
+W_READOUT = 5

@@ -366,3 +366,46 @@ def test_host_pack_pvq_fp4_valued_codebook(L):
         oi, os_ = O.pack_pvq(w, s, cb)
         assert np.array_equal(idx, oi.reshape(-1))
         assert np.array_equal(sc, os_.view(np.uint8).reshape(-1))
+
+
+def test_split_nibbles_byte_identical_to_oracle(L):
+    """lbq_split_nibbles against the oracle's nibble split and high-nibble
+    scale/zero, on packed 8-bit weights (host, byte for byte)."""
+    for n, k in [(3, 128), (37, 1024)]:
+        w = synth.weights(n, k, workload=8, item=200 + n)
+        s = synth.signs(k, workload=8, item=200 + n)
+        planes, meta = L.pack(w, 8, s)
+        hi, lo, hm = L.split_nibbles(planes, meta, k, n)
+        olo, ohi = O.split_nibbles(planes.view(np.uint32).reshape(n, -1, 8, 4))
+        assert np.array_equal(hi.view(np.uint32).reshape(ohi.shape), ohi)
+        assert np.array_equal(lo.view(np.uint32).reshape(olo.shape), olo)
+        assert np.array_equal(hm.view(np.uint16).reshape(-1), O.nibble_hi_meta(meta.view(np.uint16).reshape(-1, 2)).reshape(-1))
+
+
+def test_split_nibbles_and_readout_errors(L):
+    import ctypes
+
+    w = synth.weights(2, 128, workload=8, item=300)
+    s = synth.signs(128, workload=8, item=300)
+    planes, meta = L.pack(w, 8, s)
+    out = np.zeros(2 * 64, np.uint8)
+    hm = np.zeros(8, np.uint8)
+    f = L.lib().lbq_split_nibbles
+    assert f(None, meta.ctypes.data, 128, 2, out.ctypes.data, out.ctypes.data, hm.ctypes.data) == -1
+    assert f(planes.ctypes.data, meta.ctypes.data, 100, 2, out.ctypes.data, out.ctypes.data, hm.ctypes.data) == -2
+    bad = meta.view(np.uint16).copy()
+    bad[1] = np.float16(0.3).view(np.uint16)          # a zero that is no integer: (z - 7.5) / 16 not exact
+    assert f(planes.ctypes.data, bad.ctypes.data, 128, 2, out.ctypes.data, out.ctypes.data, hm.ctypes.data) == -6
+    r = L.Readout(128, 2, 16, 16, 16, 16, 16)           # aligned stand-in pointers: queries only
+    b = ctypes.c_size_t()
+    ws = L.lib().lbq_readout_workspace
+    assert ws(ctypes.byref(r), 1, 8, ctypes.byref(b)) == 0 and b.value > 0
+    assert ws(ctypes.byref(r), 1, 0, ctypes.byref(b)) == -2
+    assert ws(ctypes.byref(r), 1, 65, ctypes.byref(b)) == -2
+    assert ws(ctypes.byref(r), 65536, 8, ctypes.byref(b)) == -2
+    assert ws(ctypes.byref(L.Readout(100, 2, 16, 16, 16, 16, 16)), 1, 8, ctypes.byref(b)) == -2
+    assert ws(ctypes.byref(L.Readout(128, 2, 16, 16, 16, 16, 0)), 1, 8, ctypes.byref(b)) == -1
+    assert ws(ctypes.byref(L.Readout(128, 2, 8, 16, 16, 16, 16)), 1, 8, ctypes.byref(b)) == -4
+    rs = L.lib().lbq_readout_screened
+    assert rs(ctypes.byref(r), None, 0, 8, None, None, None, None, 0, None) == 0     # M = 0: no-op
+    assert rs(ctypes.byref(r), None, 1, 8, None, None, None, None, 0, None) == -1
