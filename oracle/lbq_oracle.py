@@ -470,6 +470,35 @@ def pvq_dequantize(idx: np.ndarray, scale_u16: np.ndarray, cb_bytes: np.ndarray)
     return (cb[idx.astype(np.int64)] * s[:, None, None]).reshape(n, -1)
 
 
+def pack_pvq_stages(w: np.ndarray, signs: np.ndarray, cb_bytes: np.ndarray, stages: int):
+    """Residual product-VQ at 2 * stages bits per weight (a reading of the
+    Laguna-S-2.1 card's higher-rate FP8-CB rungs: 16 index bits per 8-weight
+    vector per stage, so three stages carry the 48 bits of its 6.0-bpw rung).
+    Stage 1 encodes the rotated weight as pack_pvq does; every later stage
+    encodes what the stages before it left, w' minus their decode, with its own
+    RMS row scale and the same codebook. Returns idx uint8 [stages][N][K/4] and
+    row scales uint16 [stages][N] (fp16 bit patterns)."""
+    if stages < 1:
+        raise ValueError("stages must be at least 1")
+    res = rotate(np.asarray(w, dtype=np.float64), signs)
+    idxs, scales = [], []
+    for _ in range(stages):
+        idx, s16 = pvq_encode(res, cb_bytes)
+        res = res - pvq_dequantize(idx, s16.view(np.uint16), cb_bytes)
+        idxs.append(idx)
+        scales.append(s16.view(np.uint16))
+    return np.stack(idxs), np.stack(scales)
+
+
+def pvq_dequantize_stages(idx: np.ndarray, scale_u16: np.ndarray, cb_bytes: np.ndarray) -> np.ndarray:
+    """W'_hat = sum over stages of s_n^(t) C[idx^(t)] (float64, rotated basis)."""
+    return sum(pvq_dequantize(idx[t], scale_u16[t], cb_bytes) for t in range(idx.shape[0]))
+
+
+def linear_pvq_stages(x16, idx, scale_u16, cb_bytes, signs) -> np.ndarray:
+    return linear(x16, inverse_rotate(pvq_dequantize_stages(idx, scale_u16, cb_bytes), signs))
+
+
 def dequant_weight_pvq(idx, scale_u16, cb_bytes, signs) -> np.ndarray:
     return inverse_rotate(pvq_dequantize(idx, scale_u16, cb_bytes), signs)
 

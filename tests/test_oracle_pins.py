@@ -673,3 +673,37 @@ def test_screened_readout_exact_on_candidates_and_coarse_bound():
     xr = np.abs(O.rotate(x.astype(np.float64), sg)).reshape(m, k // 128, 128).sum(-1)   # [M][G]
     bound = 7.5 * xr @ s8.astype(np.float64).T                                          # [M][N]
     assert np.all(np.abs(full - coarse) <= bound * (1 + 1e-12))
+
+
+# ---------------------------------------------------------------- residual product-VQ stages
+
+def test_pvq_one_stage_is_plain_pvq_and_stages_telescope():
+    """One stage equals the plain encoder; with three stages every stage's
+    indices are the brute-force nearest entries of what the earlier stages
+    left (divided by that stage's RMS row scale), and the weight error falls
+    stage by stage."""
+    cb = synth.codebook(workload=9)
+    k, n = 128, 3
+    sg = synth.signs(k, workload=9, item=31)
+    w = synth.weights(n, k, workload=9, item=31)
+    i1, s1 = O.pack_pvq_stages(w, sg, cb, 1)
+    pi, ps = O.pack_pvq(w, sg, cb)
+    assert np.array_equal(i1[0], pi) and np.array_equal(s1[0], ps)
+    idx, sc = O.pack_pvq_stages(w, sg, cb, 3)
+    c = O.e4m3_to_float(cb).reshape(256, 4)
+    wrot = O.rotate(w.astype(np.float64), sg)
+    res = wrot.copy()
+    errs = []
+    for t in range(3):
+        s_t = sc[t].view(np.float16).astype(np.float64)
+        want_s = np.sqrt(np.mean(res ** 2, axis=1)) / np.sqrt(np.mean(c ** 2))
+        assert np.allclose(s_t, want_s, rtol=2 ** -10)
+        for r in range(n):
+            for i in range(k // 4):
+                a = res[r, 4 * i:4 * i + 4] / s_t[r]
+                d = [(((a[0] - e[0]) ** 2 + (a[1] - e[1]) ** 2) + (a[2] - e[2]) ** 2) + (a[3] - e[3]) ** 2 for e in c]
+                assert idx[t, r, i] == int(np.argmin(d))
+        res = res - (c[idx[t].astype(np.int64)] * s_t[:, None, None]).reshape(n, -1)
+        errs.append(np.linalg.norm(res) / np.linalg.norm(wrot))
+    assert errs[0] > errs[1] > errs[2]
+    assert np.allclose(O.pvq_dequantize_stages(idx, sc, cb) + res, wrot, rtol=0, atol=1e-12)
