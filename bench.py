@@ -28,7 +28,8 @@ the ones the counters were taken on.
 extra: every other part of the hot path, each against its own roofline: the
 single 4096x4096 linear, the stack at M = 4 and 16, the 5120/17408 FFN pair at
 M = 1, 8, 64, 256 (the TFLOP/s at M = 64 is the metric's second half), the
-product-VQ 4096->14336 linear at M = 1, 16, 64, the 256-expert MoE block at
+product-VQ 4096->14336 linear at M = 1, 16, 64 (2 and 6 bits per weight),
+the 256-expert MoE block at
 M = 32 (and its prefill at 256 and 2048 tokens), the router and the rotation
 alone, and the screened readout of an 8-bit 2048 -> 131072 vocabulary weight
 against its plain 8-bit readout.
@@ -602,14 +603,16 @@ def extra_ffn(torch, L, steps, Ms=None):
     return res
 
 
-def extra_pvq(torch, L, steps, Ms=None):
+def extra_pvq(torch, L, steps, Ms=None, bits=2):
+    """The product-VQ linear 4096 -> 14336; bits 4 and 6 are two and three
+    residual stages (idx and row scales per stage)."""
     cfg = synth.PVQ_LINEAR
     cb = synth.codebook(workload=synth.W_PVQ)
     w = synth.weights(cfg["N"], cfg["K"], workload=synth.W_PVQ)
     s = synth.signs(cfg["K"], workload=synth.W_PVQ)
-    idx, sc = L.pack(w, 2, s, L.FMT_PVQ_4x8, cb)
+    idx, sc = L.pack(w, bits, s, L.FMT_PVQ_4x8, cb)
     del w
-    lin = Linears(L, torch, cfg["K"], cfg["N"], 2, L.FMT_PVQ_4x8, idx, sc, s, cb,
+    lin = Linears(L, torch, cfg["K"], cfg["N"], bits, L.FMT_PVQ_4x8, idx, sc, s, cb,
                   copies_for(idx.nbytes + sc.nbytes + cb.nbytes))
     res = {f"M{M}": measure_linears(torch, L, lin, M, steps, workload=synth.W_PVQ) for M in (Ms or cfg["M"])}
     del lin
@@ -1052,7 +1055,7 @@ def planes_meta_bytes(k, n, bits):
 # ---------------------------------------------------------------- main
 
 CASES = ("stack1", "stack4", "stack16", "single", "ffn1", "ffn8", "ffn64", "ffn256", "pvq1", "pvq16", "pvq64", "moe",
-         "moe256", "moe2048", "readout1", "readout4")
+         "moe256", "moe2048", "readout1", "readout4", "pvq6bpw1", "pvq6bpw16", "pvq6bpw64")
 
 
 def run_case(torch, L, case, steps):
@@ -1064,6 +1067,8 @@ def run_case(torch, L, case, steps):
         r = extra_single(torch, L, steps)
     elif case.startswith("ffn"):
         r = extra_ffn(torch, L, steps, Ms=(int(case[3:]),))
+    elif case.startswith("pvq6bpw"):
+        r = extra_pvq(torch, L, steps, Ms=(int(case[7:]),), bits=6)
     elif case.startswith("pvq"):
         r = extra_pvq(torch, L, steps, Ms=(int(case[3:]),))
     elif case.startswith("readout"):
@@ -1197,6 +1202,8 @@ def main():
         extra["ffn_pair"] = extra_ffn(torch, L, steps)
         log("[bench] extra: product-VQ 4096->14336")
         extra["pvq"] = extra_pvq(torch, L, steps)
+        log("[bench] extra: product-VQ 4096->14336 at 6 bits per weight (three residual stages)")
+        extra["pvq_6bpw"] = extra_pvq(torch, L, steps, bits=6)
         log("[bench] extra: MoE block")
         extra["moe_block"] = extra_moe(torch, L, steps)
         for M in (256, 2048):

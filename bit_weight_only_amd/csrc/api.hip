@@ -26,7 +26,7 @@ lbq_status check_weight(const lbq_weight *w) {
     if ((w->bits < 2 || w->bits > 4) && w->bits != 8) return LBQ_ERR_BITS;
   } else if (w->format == LBQ_FMT_PVQ_4x8) {
     if (!w->codebook) return LBQ_ERR_NULL;
-    if (w->bits != 2) return LBQ_ERR_BITS;
+    if (w->bits != 2 && w->bits != 4 && w->bits != 6) return LBQ_ERR_BITS;   // 1, 2, 3 residual stages
   } else {
     return LBQ_ERR_FORMAT;
   }
@@ -72,17 +72,20 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
       (w->bits != 8 || gemv_mfma_supported_8bit(w->K, w->N)))
     return hip_status(launch_gemv_mfma(w->planes, w->meta, x, w->signs, y, M, w->K, w->N, w->bits, 0, 0, 0, s, ev0,
                                        ev1));
-  if (w->format == LBQ_FMT_PVQ_4x8 && gemv && gemv_pvq_mx_supported(M, w->K, w->N) && aligned16(w->signs) &&
+  const int stages = w->format == LBQ_FMT_PVQ_4x8 ? w->bits / 2 : 1;
+  if (w->format == LBQ_FMT_PVQ_4x8 && gemv && gemv_pvq_mx_supported(M, w->K, w->N, stages) && aligned16(w->signs) &&
       (reinterpret_cast<uintptr_t>(w->codebook) & 3u) == 0) {
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return LBQ_ERR_HIP;
     if (launch_gemv_pvq_mx(static_cast<const uint8_t *>(w->planes), static_cast<const uint16_t *>(w->meta),
-                           static_cast<const uint8_t *>(w->codebook), x, w->signs, y, M, w->K, w->N, s) != hipSuccess)
+                           static_cast<const uint8_t *>(w->codebook), x, w->signs, y, M, w->K, w->N, stages,
+                           s) != hipSuccess)
       return LBQ_ERR_HIP;
     return (ev1 && hipEventRecord(ev1, s) != hipSuccess) ? LBQ_ERR_HIP : LBQ_OK;
   }
   uint16_t *xr = static_cast<uint16_t *>(ws);
-  // 8-bit codes run on the matrix-core GEMV or the MFMA GEMM only
-  if (gemv && w->format == LBQ_FMT_RTN_PLANES && w->bits == 8) {
+  // 8-bit codes and residual product-VQ stages run on the matrix-core GEMV or
+  // the MFMA GEMM only
+  if (gemv && ((w->format == LBQ_FMT_RTN_PLANES && w->bits == 8) || stages > 1)) {
     if (path == LBQ_PATH_GEMV) return LBQ_ERR_SHAPE;
     gemv = false;
   }
@@ -102,7 +105,7 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
     const hipError_t ge =
         rtn ? launch_gemm_rtn(gp, w->bits, w->planes, w->meta, xr, tz, y, M, w->K, w->N, scratch, s)
             : launch_gemm_pvq(gp, w->planes, w->meta, static_cast<const uint8_t *>(w->codebook), xr, y, M, w->K, w->N,
-                              scratch, s);
+                              stages, scratch, s);
     if (ge != hipSuccess) return LBQ_ERR_HIP;
     return (ev1 && hipEventRecord(ev1, s) != hipSuccess) ? LBQ_ERR_HIP : LBQ_OK;
   }
@@ -143,7 +146,7 @@ lbq_status lbq_packed_bytes(int32_t K, int32_t N, int32_t bits, int32_t format, 
   if (format == LBQ_FMT_RTN_PLANES) {
     if ((bits < 2 || bits > 4) && bits != 8) return LBQ_ERR_BITS;
   } else if (format == LBQ_FMT_PVQ_4x8) {
-    if (bits != 2) return LBQ_ERR_BITS;
+    if (bits != 2 && bits != 4 && bits != 6) return LBQ_ERR_BITS;
   } else {
     return LBQ_ERR_FORMAT;
   }
@@ -151,9 +154,9 @@ lbq_status lbq_packed_bytes(int32_t K, int32_t N, int32_t bits, int32_t format, 
   if (format == LBQ_FMT_RTN_PLANES) {
     *plane_bytes = static_cast<size_t>(N) * K / 8 * bits;
     *meta_bytes = static_cast<size_t>(N) * (K / 128) * 4;
-  } else {
-    *plane_bytes = static_cast<size_t>(N) * (K / 4);
-    *meta_bytes = static_cast<size_t>(N) * 2;
+  } else {   // bits / 2 residual stages of indices and row scales
+    *plane_bytes = static_cast<size_t>(bits / 2) * N * (K / 4);
+    *meta_bytes = static_cast<size_t>(bits / 2) * N * 2;
   }
   return LBQ_OK;
 }
@@ -169,7 +172,8 @@ lbq_status lbq_pack(const float *W, int32_t K, int32_t N, int32_t bits, int32_t 
   if (format == LBQ_FMT_RTN_PLANES)
     return pack_rtn(W, K, N, bits, signs, static_cast<uint32_t *>(planes_out), static_cast<uint16_t *>(meta_out));
   if (!codebook) return LBQ_ERR_NULL;
-  return pack_pvq(W, K, N, signs, codebook, static_cast<uint8_t *>(planes_out), static_cast<uint16_t *>(meta_out));
+  return pack_pvq(W, K, N, signs, codebook, static_cast<uint8_t *>(planes_out), static_cast<uint16_t *>(meta_out),
+                  bits / 2);
 }
 
 lbq_status lbq_gptq_factor(const double *H, int32_t K, const int8_t *signs, double damp, double *U) {
@@ -285,7 +289,7 @@ lbq_status lbq_unpack_codes(const lbq_weight *w, uint8_t *codes, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w->format == LBQ_FMT_RTN_PLANES)
     return hip_status(launch_unpack_rtn(w->planes, w->K, w->N, w->bits, codes, s));
-  return hip_status(hipMemcpyAsync(codes, w->planes, static_cast<size_t>(w->N) * (w->K / 4),
+  return hip_status(hipMemcpyAsync(codes, w->planes, static_cast<size_t>(w->bits / 2) * w->N * (w->K / 4),
                                    hipMemcpyDeviceToDevice, s));
 }
 

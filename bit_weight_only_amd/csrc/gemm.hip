@@ -46,23 +46,45 @@ constexpr int kThreads = 64 * kWaves;
 // of the lane set copied by lane (j, u). Lane (j, kq) needs word column kq
 // (index bytes 8kq..8kq+7, weights 32kq..32kq+31): half kq & 1 of vector
 // 2 nb + (kq >> 1).
-template <int NB>
+// ST residual stages (stage t's indices at idx + t N K / 4, its row scales at
+// row_scale + t N) fold into one fp16 B value per weight:
+// C[i_1] + r_2 C[i_2] + r_3 C[i_3], r_t the fp16 ratio of stage t's row scale
+// to stage 1's (two fused multiply-adds per weight pair); stage 1's row scale
+// is applied at the end as for one stage.
+template <int NB, int ST>
 struct PvqTile {
   static constexpr int V = 2 * NB;
   static constexpr int T = (V + 3) / 4;
-  static constexpr int kDma = T;
-  static constexpr int kBVecs = 64 * T;
-  const uint8_t *idx;      // [N][K/4]
+  static constexpr int kDma = T * ST;
+  static constexpr int kBVecs = 64 * T;          // per wave and stage
+  const uint8_t *idx;      // [ST][N][K/4]
   const uint32_t *lut;     // LDS: 256 entries x 2 u32 (4 fp16)
   int K, N;
+  half2_t r[NB][ST > 1 ? ST : 1];   // stage ratios of this lane's rows (entry 0 unused)
+  __device__ __forceinline__ void prepare(const uint16_t *row_scale, int row0) {
+    if constexpr (ST > 1) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int row = min(row0 + nb * 16, N - 1);
+        const float s1 = f16_bits_to_f32(row_scale[row]);
+#pragma unroll
+        for (int st = 1; st < ST; ++st) {
+          const _Float16 q = static_cast<_Float16>(f16_bits_to_f32(row_scale[static_cast<size_t>(st) * N + row]) / s1);
+          r[nb][st] = half2_t{q, q};
+        }
+      }
+    }
+  }
   __device__ __forceinline__ void request(uint4 *bslot, int row0, int g, int kq, int wave) const {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int u = min(kq + 4 * t, V - 1);
-      const int row = min(row0 + (u >> 1) * 16, N - 1);
-      copy16_to_lds(idx + static_cast<size_t>(row) * (K / 4) + g * 32 + (u & 1) * 16,
-                      bslot + kBVecs * wave + 64 * t);
-    }
+    for (int st = 0; st < ST; ++st)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int u = min(kq + 4 * t, V - 1);
+        const int row = min(row0 + (u >> 1) * 16, N - 1);
+        copy16_to_lds(idx + (static_cast<size_t>(st) * N + row) * (K / 4) + g * 32 + (u & 1) * 16,
+                      bslot + kBVecs * (kWaves * st + wave) + 64 * t);
+      }
   }
   // slot c = (w[c], w[c+16]); weights 4t..4t+3 use index byte t, weights
   // 16+4t.. use index byte t+4.
@@ -71,17 +93,29 @@ struct PvqTile {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int u = 2 * nb + (kq >> 1);
-      const uint2 w = reinterpret_cast<const uint2 *>(bslot + kBVecs * wave + 64 * (u >> 2) + (u & 3) * 16 + j)[kq & 1];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t ia = (w.x >> (8 * t)) & 0xFFu;
-        const uint32_t ib = (w.y >> (8 * t)) & 0xFFu;
-        const uint2 ca = *reinterpret_cast<const uint2 *>(lut + 2 * ia);
-        const uint2 cb = *reinterpret_cast<const uint2 *>(lut + 2 * ib);
-        b[nb][4 * t + 0] = (ca.x & 0xFFFFu) | (cb.x << 16);
-        b[nb][4 * t + 1] = (ca.x >> 16) | (cb.x & 0xFFFF0000u);
-        b[nb][4 * t + 2] = (ca.y & 0xFFFFu) | (cb.y << 16);
-        b[nb][4 * t + 3] = (ca.y >> 16) | (cb.y & 0xFFFF0000u);
+      for (int st = 0; st < ST; ++st) {
+        const uint2 w = reinterpret_cast<const uint2 *>(bslot + kBVecs * (kWaves * st + wave) + 64 * (u >> 2) +
+                                                         (u & 3) * 16 + j)[kq & 1];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t ia = (w.x >> (8 * t)) & 0xFFu;
+          const uint32_t ib = (w.y >> (8 * t)) & 0xFFu;
+          const uint2 ca = *reinterpret_cast<const uint2 *>(lut + 2 * ia);
+          const uint2 cb = *reinterpret_cast<const uint2 *>(lut + 2 * ib);
+          const uint32_t v[4] = {(ca.x & 0xFFFFu) | (cb.x << 16), (ca.x >> 16) | (cb.x & 0xFFFF0000u),
+                                 (ca.y & 0xFFFFu) | (cb.y << 16), (ca.y >> 16) | (cb.y & 0xFFFF0000u)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (st == 0) {
+              b[nb][4 * t + e] = v[e];
+            } else {
+              b[nb][4 * t + e] = __builtin_bit_cast(
+                  uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, v[e]), r[nb][st > 0 ? st : 0],
+                                                      __builtin_bit_cast(half2_t, b[nb][4 * t + e])));
+            }
+          }
+        }
       }
     }
   }
@@ -116,8 +150,8 @@ struct Ring {
   uint4 *b[R];
 };
 
-template <int NB, int MT, int R>
-__device__ __forceinline__ void gemm_body(const PvqTile<NB> &tile, const GemmArgs &a, const Ring<R> &ring) {
+template <int NB, int ST, int MT, int R>
+__device__ __forceinline__ void gemm_body(const PvqTile<NB, ST> &tile, const GemmArgs &a, const Ring<R> &ring) {
   constexpr int CA = MT;   // activation copies per wave per group
   const int G = a.K / kGroup;
   const int lane = threadIdx.x & 63;
@@ -153,7 +187,7 @@ __device__ __forceinline__ void gemm_body(const PvqTile<NB> &tile, const GemmArg
     for (int i = 0; i < CA; ++i) copy16_to_lds(asrc[i] + static_cast<size_t>(gc) * 16, ring.a[q] + 64 * (CA * wave + i));
     tile.request(ring.b[q], row0, gc, kq, wave);
   };
-  constexpr int kCopies = CA + PvqTile<NB>::kDma;   // per wave per group
+  constexpr int kCopies = CA + PvqTile<NB, ST>::kDma;   // per wave per group
 
   auto contract = [&](int q) {
     uint32_t b[NB][16];
@@ -247,14 +281,14 @@ __device__ __forceinline__ void gemm_body(const PvqTile<NB> &tile, const GemmArg
 
 // The ring slots are separate LDS objects so the compiler can tell that a
 // read of one slot does not depend on the copies in flight into the others.
-template <int NB, int MT>
+template <int NB, int ST, int MT>
 __global__ void __launch_bounds__(kThreads) gemm_pvq_kernel(const uint8_t *__restrict__ idx,
                                                             const uint8_t *__restrict__ codebook, GemmArgs a) {
-  using Tile = PvqTile<NB>;
+  using Tile = PvqTile<NB, ST>;
   constexpr int R = ring_depth<MT>();
-#define LBQ_SLOT(I)                                                   \
-  __shared__ __attribute__((aligned(16))) uint4 a##I[16 * MT * 16];  \
-  __shared__ __attribute__((aligned(16))) uint4 b##I[kWaves * Tile::kBVecs];
+#define LBQ_SLOT(I)                                                                      \
+  __shared__ __attribute__((aligned(16))) uint4 a##I[(I) < R ? 16 * MT * 16 : 1];        \
+  __shared__ __attribute__((aligned(16))) uint4 b##I[(I) < R ? kWaves * ST * Tile::kBVecs : 1];
   LBQ_SLOT(0) LBQ_SLOT(1) LBQ_SLOT(2) LBQ_SLOT(3)
 #undef LBQ_SLOT
   Ring<R> ring;
@@ -276,17 +310,25 @@ __global__ void __launch_bounds__(kThreads) gemm_pvq_kernel(const uint8_t *__res
     lut[e] = out;
   }
   __syncthreads();
-  Tile tile{idx, lut, a.K, a.N};
-  gemm_body<NB, MT, R>(tile, a, ring);
+  Tile tile{idx, lut, a.K, a.N, {}};
+  tile.prepare(a.row_scale, blockIdx.y * (kWaves * 16 * NB) + (threadIdx.x >> 6) * 16 * NB + (threadIdx.x & 15));
+  gemm_body<NB, ST, MT, R>(tile, a, ring);
 }
 
-template <int NB>
+template <int NB, int ST>
 void launch_pvq_nb(int mt, dim3 grid, const uint8_t *idx, const uint8_t *codebook, const GemmArgs &a, hipStream_t s) {
   switch (mt) {
-    case 1: hipLaunchKernelGGL((gemm_pvq_kernel<NB, 1>), grid, dim3(kThreads), 0, s, idx, codebook, a); break;
-    case 2: hipLaunchKernelGGL((gemm_pvq_kernel<NB, 2>), grid, dim3(kThreads), 0, s, idx, codebook, a); break;
-    default: hipLaunchKernelGGL((gemm_pvq_kernel<NB, 4>), grid, dim3(kThreads), 0, s, idx, codebook, a); break;
+    case 1: hipLaunchKernelGGL((gemm_pvq_kernel<NB, ST, 1>), grid, dim3(kThreads), 0, s, idx, codebook, a); break;
+    case 2: hipLaunchKernelGGL((gemm_pvq_kernel<NB, ST, 2>), grid, dim3(kThreads), 0, s, idx, codebook, a); break;
+    default: hipLaunchKernelGGL((gemm_pvq_kernel<NB, ST, 4>), grid, dim3(kThreads), 0, s, idx, codebook, a); break;
   }
+}
+
+template <int ST>
+void launch_pvq_st(int nb, int mt, dim3 grid, const uint8_t *idx, const uint8_t *codebook, const GemmArgs &a,
+                   hipStream_t s) {
+  if (nb == 1) launch_pvq_nb<1, ST>(mt, grid, idx, codebook, a, s);
+  else launch_pvq_nb<2, ST>(mt, grid, idx, codebook, a, s);
 }
 
 }  // namespace
@@ -390,9 +432,11 @@ uint32_t *gemm_counter_ptr(const GemmPlan &p, void *scratch) {
 }
 
 hipError_t launch_gemm_pvq(const GemmPlan &p, const void *idx, const void *row_scale, const uint8_t *codebook,
-                           const uint16_t *xf, uint16_t *y, int M, int K, int N, void *scratch, hipStream_t s) {
+                           const uint16_t *xf, uint16_t *y, int M, int K, int N, int stages, void *scratch,
+                           hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if ((p.nb != 1 && p.nb != 2) || (p.mt != 1 && p.mt != 2 && p.mt != 4) || p.S < 1) return hipErrorInvalidValue;
+  if (stages < 1 || stages > 3 || static_cast<long long>(stages) * N * (K / 4) >= (1ll << 31)) return hipErrorInvalidValue;
   GemmArgs a;
   a.xf = reinterpret_cast<const uint4 *>(xf);
   a.y = y;
@@ -405,8 +449,9 @@ hipError_t launch_gemm_pvq(const GemmPlan &p, const void *idx, const void *row_s
   a.S = p.S;
   const dim3 grid(static_cast<unsigned>(p.S), static_cast<unsigned>(p.n_tiles), static_cast<unsigned>(p.m_tiles));
   const uint8_t *ix = static_cast<const uint8_t *>(idx);
-  if (p.nb == 1) launch_pvq_nb<1>(p.mt, grid, ix, codebook, a, s);
-  else launch_pvq_nb<2>(p.mt, grid, ix, codebook, a, s);
+  if (stages == 1) launch_pvq_st<1>(p.nb, p.mt, grid, ix, codebook, a, s);
+  else if (stages == 2) launch_pvq_st<2>(p.nb, p.mt, grid, ix, codebook, a, s);
+  else launch_pvq_st<3>(p.nb, p.mt, grid, ix, codebook, a, s);
   return hipGetLastError();
 }
 

@@ -58,9 +58,10 @@ hipError_t launch_gemv_pvq(const uint8_t *idx, const uint16_t *scale, const uint
 // cores (fp8 activation pieces x fp8 codebook values), rotation fused into the
 // prologue: one launch, no workspace. x and signs 16-byte aligned, codebook
 // 4-byte aligned.
-bool gemv_pvq_mx_supported(int M, int K, int N);
+// stages: residual product-VQ stages (idx [stages][N][K/4], row_scale [stages][N]).
+bool gemv_pvq_mx_supported(int M, int K, int N, int stages);
 hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, const uint8_t *codebook,
-                              const uint16_t *x, const int8_t *signs, uint16_t *y, int M, int K, int N,
+                              const uint16_t *x, const int8_t *signs, uint16_t *y, int M, int K, int N, int stages,
                               hipStream_t s);
 // MFMA dequant-GEMMs on activations rotated into the folded slot order
 // (launch_rotate_folded): RTN planes (gemm_rtn_plan, launch_gemm_rtn, with the
@@ -106,7 +107,8 @@ struct GroupedGemm {
 };
 hipError_t launch_gemm_rtn_grouped(const GroupedGemm &g, hipStream_t s);
 hipError_t launch_gemm_pvq(const GemmPlan &p, const void *idx, const void *row_scale, const uint8_t *codebook,
-                           const uint16_t *xf, uint16_t *y, int M, int K, int N, void *scratch, hipStream_t s);
+                           const uint16_t *xf, uint16_t *y, int M, int K, int N, int stages, void *scratch,
+                           hipStream_t s);
 
 // Measurement reference: read bytes (a multiple of 16) at buf once in one
 // launch of grid x block threads; non-null events take the kernel's own

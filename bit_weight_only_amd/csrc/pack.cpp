@@ -207,7 +207,7 @@ lbq_status pack_rtn(const float *W, int K, int N, int bits, const int8_t *signs,
 }
 
 lbq_status pack_pvq(const float *W, int K, int N, const int8_t *signs, const uint8_t *codebook,
-                    uint8_t *idx, uint16_t *scale) {
+                    uint8_t *idx, uint16_t *scale, int stages) {
   double cb[256][4];
   double sum_c = 0.0;
   for (int j = 0; j < 256; ++j) {
@@ -231,6 +231,8 @@ lbq_status pack_pvq(const float *W, int K, int N, const int8_t *signs, const uin
         v[k] = static_cast<double>(w[k]);
       }
       rotate_row(v.data(), signs, K);
+      // stage t encodes what stages 0..t-1 left in v (residual product-VQ)
+      for (int t = 0; t < stages; ++t) {
       double sum_w = 0.0;
       for (int k = 0; k < K; ++k) sum_w += v[k] * v[k];
       const double ratio = std::sqrt(sum_w / K) / std::sqrt(sum_c / 1024.0);
@@ -240,9 +242,9 @@ lbq_status pack_pvq(const float *W, int K, int N, const int8_t *signs, const uin
         return;
       }
       if (s16 == 0) s16 = 0x3C00u;
-      scale[n] = s16;
+      scale[static_cast<size_t>(t) * N + n] = s16;
       const double s = f16_to_f64(s16);
-      uint8_t *out = idx + static_cast<size_t>(n) * (K / 4);
+      uint8_t *out = idx + (static_cast<size_t>(t) * N + n) * (K / 4);
       for (int i = 0; i < K / 4; ++i) {
         const double a0 = v[4 * i] / s, a1 = v[4 * i + 1] / s, a2 = v[4 * i + 2] / s, a3 = v[4 * i + 3] / s;
         double best = INFINITY;
@@ -259,6 +261,8 @@ lbq_status pack_pvq(const float *W, int K, int N, const int8_t *signs, const uin
           }
         }
         out[i] = static_cast<uint8_t>(bj);
+        for (int d = 0; d < 4; ++d) v[4 * i + d] -= cb[bj][d] * s;
+      }
       }
     }
   });

@@ -25,9 +25,10 @@ void store_group(const uint8_t q[128], int bits, uint16_t s16, uint16_t z16, uin
 lbq_status pack_rtn(const float *W, int K, int N, int bits, const int8_t *signs, uint32_t *planes,
                     uint16_t *meta);
 
-// Product-VQ packing of W [N][K] into idx [N][K/4] and fp16 row scales [N].
+// Product-VQ packing of W [N][K] into idx [stages][N][K/4] and fp16 row
+// scales [stages][N]: stage t encodes the residual the earlier stages left.
 lbq_status pack_pvq(const float *W, int K, int N, const int8_t *signs, const uint8_t *codebook,
-                    uint8_t *idx, uint16_t *scale);
+                    uint8_t *idx, uint16_t *scale, int stages);
 
 // GPTQ: the upper Cholesky factor U of (R H R^T + damp mean(diag) I)^-1 of a
 // host Hessian H [K][K] (original basis), and packing with error feedback

@@ -18,6 +18,9 @@
 // Work split as in the RTN matrix-core GEMV: items of (16-row tile, batch of
 // two groups) round-robin over the waves, partial sums per wave in LDS added
 // in wave order at the end (repeat calls are bit-identical).
+// Residual stages (idx [S][N][K/4], row scales [S][N]): a workgroup's tiles
+// are walked once per stage (stage-major "virtual tiles"), each with its own
+// partial sums, and y = sum over stages of the stage's row scale times them.
 #include "kernels.h"
 #include "mx_core.h"
 
@@ -64,28 +67,31 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
                                                                   const uint32_t *__restrict__ codebook,
                                                                   const uint4 *__restrict__ x,
                                                                   const uint4 *__restrict__ signs,
-                                                                  uint16_t *__restrict__ y, const MxShape sh) {
+                                                                  uint16_t *__restrict__ y, const MxShape sh,
+                                                                  const int stages_arg) {
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   const int M = sh.M, K = sh.K, N = sh.N, G = sh.G, Gp = sh.Gp;
   const int VR = G * 2;                          // 16-byte index vectors per row
   const int b = static_cast<int>(blockIdx.x);
   const int ntl = sh.tq + (b < sh.tr ? 1 : 0);   // this workgroup's tiles: b + k grid, k < ntl
   const int rows = ntl * 16;
-  const int items = ntl * sh.NB;
+  const int stages = stages_arg;
+  const int vrows = stages * rows;               // partial-sum rows: stage-major virtual tiles
+  const int items = stages * ntl * sh.NB;
   const int nw = static_cast<int>(blockDim.x >> 6), nt = static_cast<int>(blockDim.x);
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));   // wave-uniform
   const int lane = static_cast<int>(threadIdx.x & 63), j = lane & 15, kq = lane >> 4;
   const uint32_t lcopy = static_cast<uint32_t>(lane) & (kLutCopies - 1);   // this lane's codebook copy
 
   // LDS: codebook [256][kLutCopies] words, piece sets [M][Gp], A-scale
-  // exponents [M][Gp], the waves' row partial sums [nw][M][rows].
+  // exponents [M][Gp], the waves' row partial sums [nw][M][stages * rows].
   uint32_t *lut = smem;
   uint32_t *xa = smem + 256 * kLutCopies;
   uint32_t *sx = xa + M * Gp * (kSetBytes / 4);
   float *yl = reinterpret_cast<float *>(sx + M * Gp);
 
   const __amdgpu_buffer_rsrc_t prs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4 *>(idx), 0, N * VR * 16, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4 *>(idx), 0, stages * N * VR * 16, kBufferFlags);
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4 *>(x), 0, M * K * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t srs =
@@ -101,7 +107,13 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
   MxCursor pc = lc;
   auto load = [&](uint4 &it) {
     const uint32_t past = lc.i < items ? 0u : kOutOfRange;
-    const uint32_t pstep = static_cast<uint32_t>((lc.tile * tstride * VR + lc.batch * kGB * 2) * 16) + past;
+    int st = 0, tl = lc.tile;   // virtual tile -> (stage, tile)
+    while (tl >= ntl && st + 1 < stages) {
+      tl -= ntl;
+      ++st;
+    }
+    const uint32_t pstep =
+        static_cast<uint32_t>((tl * tstride * VR + lc.batch * kGB * 2) * 16 + st * N * VR * 16) + past;
     it = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, pbase + pstep, 0, 0));
     lc.advance(sh, nw);
   };
@@ -164,7 +176,7 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
       reinterpret_cast<uint4 *>(xa + q * (kSetBytes / 4) + piece_offset(3) / 4)[i - q * (kPieceBytes / 16)] =
           make_uint4(0, 0, 0, 0);
     }
-    for (int i = static_cast<int>(threadIdx.x); i < nw * M * rows; i += nt) yl[i] = 0.f;
+    for (int i = static_cast<int>(threadIdx.x); i < nw * M * vrows; i += nt) yl[i] = 0.f;
   }
   __syncthreads();
 
@@ -176,7 +188,7 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
   const uint32_t *sxl = sx + min(at, M - 1) * Gp;   // A-scale exponents of this lane's token
   const char *lds = reinterpret_cast<const char *>(xa);   // a_base is a byte offset into the piece sets
   const bool t_ok = kq < M;
-  float *ylane = yl + (wv * M + kq) * rows + j;   // this wave's partial sums (one per tile it touches)
+  float *ylane = yl + (wv * M + kq) * vrows + j;   // this wave's partial sums (one per tile it touches)
 
   v4f_t acc = {0.f, 0.f, 0.f, 0.f};
   auto process = [&](const uint4 &it) {
@@ -220,17 +232,24 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
     }
   }
   __syncthreads();
-  // the waves' partials summed in wave order, times the row scale
+  // the waves' partials summed in wave order, times each stage's row scale,
+  // stages added in order
   for (int i2 = static_cast<int>(threadIdx.x); i2 < M * rows; i2 += nt) {
     const int m = i2 / rows, r = i2 - m * rows, row = (b + (r >> 4) * sh.grid) * 16 + (r & 15);
-    float s = 0.f;
-    for (int w2 = 0; w2 < nw; ++w2) s += yl[w2 * M * rows + i2];
-    if (row < N) y[static_cast<size_t>(m) * N + row] = f32_to_f16_bits(s * f16_bits_to_f32(row_scale[row]));
+    if (row >= N) continue;
+    float out = 0.f;
+    for (int st = 0; st < stages; ++st) {
+      float s = 0.f;
+      for (int w2 = 0; w2 < nw; ++w2) s += yl[(w2 * M + m) * vrows + st * rows + r];
+      out += s * f16_bits_to_f32(row_scale[static_cast<size_t>(st) * N + row]);
+    }
+    y[static_cast<size_t>(m) * N + row] = f32_to_f16_bits(out);
   }
 }
 
-size_t pvq_mx_lds(int M, int G, int rows, int block) {
-  return 1024 * kLutCopies + static_cast<size_t>(M) * G * (kSetBytes + 4) + static_cast<size_t>(block / 64) * M * rows * 4;
+size_t pvq_mx_lds(int M, int G, int rows, int block, int stages) {
+  return 1024 * kLutCopies + static_cast<size_t>(M) * G * (kSetBytes + 4) +
+         static_cast<size_t>(block / 64) * M * stages * rows * 4;
 }
 
 constexpr int kComputeUnits = 256;
@@ -246,24 +265,25 @@ int pvq_mx_block(int N) { return (N + 15) / 16 <= kComputeUnits ? 512 : kPvqMaxT
 
 }  // namespace
 
-bool gemv_pvq_mx_supported(int M, int K, int N) {
+bool gemv_pvq_mx_supported(int M, int K, int N, int stages) {
   // K a multiple of 512: whole items of two groups, no padding groups
-  if (M < 1 || M > 4 || K < 4 * kGroup || K % (4 * kGroup) != 0 || N < 1) return false;
-  if (static_cast<long long>(N + 16) * (K / kGroup) * 32 >= static_cast<long long>(kOutOfRange)) return false;
+  if (M < 1 || M > 4 || K < 4 * kGroup || K % (4 * kGroup) != 0 || N < 1 || stages < 1 || stages > 3) return false;
+  if (static_cast<long long>(stages) * (N + 16) * (K / kGroup) * 32 >= static_cast<long long>(kOutOfRange))
+    return false;
   const int grid = pvq_mx_grid(N), T = (N + 15) / 16;
-  return pvq_mx_lds(M, K / kGroup, ((T + grid - 1) / grid) * 16, pvq_mx_block(N)) <= kMaxLds;
+  return pvq_mx_lds(M, K / kGroup, ((T + grid - 1) / grid) * 16, pvq_mx_block(N), stages) <= kMaxLds;
 }
 
 hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, const uint8_t *codebook,
-                              const uint16_t *x, const int8_t *signs, uint16_t *y, int M, int K, int N,
+                              const uint16_t *x, const int8_t *signs, uint16_t *y, int M, int K, int N, int stages,
                               hipStream_t s) {
   if ((reinterpret_cast<uintptr_t>(signs) & 15u) != 0 || (reinterpret_cast<uintptr_t>(x) & 15u) != 0 ||
-      (reinterpret_cast<uintptr_t>(codebook) & 3u) != 0 || !gemv_pvq_mx_supported(M, K, N))
+      (reinterpret_cast<uintptr_t>(codebook) & 3u) != 0 || !gemv_pvq_mx_supported(M, K, N, stages))
     return hipErrorInvalidValue;
   const int grid = pvq_mx_grid(N);
   const int block = pvq_mx_block(N);
   const MxShape sh = make_shape(M, K, N, 2, grid, block);   // batches of two groups
-  const size_t lds = pvq_mx_lds(M, sh.G, (sh.tq + (sh.tr ? 1 : 0)) * 16, block);
+  const size_t lds = pvq_mx_lds(M, sh.G, (sh.tq + (sh.tr ? 1 : 0)) * 16, block, stages);
   auto kern = gemv_pvq_mx_kernel<2>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -272,7 +292,7 @@ hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, con
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(block), lds, s, reinterpret_cast<const uint4 *>(idx), row_scale,
                      reinterpret_cast<const uint32_t *>(codebook), reinterpret_cast<const uint4 *>(x),
-                     reinterpret_cast<const uint4 *>(signs), y, sh);
+                     reinterpret_cast<const uint4 *>(signs), y, sh, stages);
   return hipGetLastError();
 }
 

@@ -244,10 +244,11 @@ def rotate(x, signs, out=None, stream=None):
 def unpack_codes(w: PackedLinear, stream=None):
     import torch
 
-    n = w.N * w.K if w.fmt == FMT_RTN_PLANES else w.N * (w.K // 4)
+    # RTN: codes [N][K]; product-VQ: indices [stages * N][K/4] (stage-major)
+    n = w.N * w.K if w.fmt == FMT_RTN_PLANES else (w.bits // 2) * w.N * (w.K // 4)
     codes = torch.empty(n, dtype=torch.uint8, device=w.planes.device)
     _check(lib().lbq_unpack_codes(ctypes.byref(w.struct), _ptr(codes), _stream(stream)), "lbq_unpack_codes")
-    return codes.view(w.N, -1)
+    return codes.view(w.N, -1) if w.fmt == FMT_RTN_PLANES else codes.view(-1, w.K // 4)
 
 
 # ------------------------------------------------------------------ screened readout

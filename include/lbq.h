@@ -47,12 +47,17 @@
  *     meta:   [N][G] pairs of IEEE fp16 (scale s, zero z), s at the lower
  *             address. meta_bytes = 4*N*G.
  *     Decoded rotated weight: W'[n][k] = (q[n][k] - z[n][g]) * s[n][g].
- *   LBQ_FMT_PVQ_4x8 (2 bits per weight):
- *     planes: uint8 idx [N][K/4]; byte i holds the codebook index of weights
- *             4i..4i+3 (byte 2v+h is half h of 8-weight vector v).
- *     meta:   fp16 row scale [N].
- *     codebook: 256 entries x 4 fp8 e4m3 (OCP "fn") bytes, row-major.
- *     Decoded rotated weight: W'[n][4i+d] = s[n] * C[idx[n][i]][d].
+ *   LBQ_FMT_PVQ_4x8, bits b in {2,4,6} = 2 per residual stage, S = b/2:
+ *     planes: uint8 idx [S][N][K/4]; byte i of a row holds the codebook index
+ *             of weights 4i..4i+3 (byte 2v+h is half h of 8-weight vector v).
+ *     meta:   fp16 row scales [S][N].
+ *     codebook: 256 entries x 4 fp8 e4m3 (OCP "fn") bytes, row-major, shared by
+ *             every stage (values on the e4m3 grid, or on the NVFP4 e2m1 grid
+ *             held as e4m3 bytes).
+ *     Decoded rotated weight: W'[n][4i+d] = sum_t s_t[n] * C[idx_t[n][i]][d].
+ *     (Laguna-S-2.1 card: product-VQ over 8-weight vectors with fp8- or
+ *     NVFP4-grid codebooks; three stages carry the 48 index bits per vector of
+ *     its 6.0-bpw FP8-CB rung.)
  */
 #ifndef LBQ_H
 #define LBQ_H
@@ -68,7 +73,7 @@ typedef enum {
   LBQ_OK = 0,
   LBQ_ERR_NULL = -1,       /* a required pointer is NULL */
   LBQ_ERR_SHAPE = -2,      /* K not a positive multiple of 128, N <= 0, M < 0, top_k outside [1, E], ... */
-  LBQ_ERR_BITS = -3,       /* bits outside {2,3,4,8} (RTN) or != 2 (PVQ) */
+  LBQ_ERR_BITS = -3,       /* bits outside {2,3,4,8} (RTN) or {2,4,6} (PVQ) */
   LBQ_ERR_ALIGN = -4,      /* a pointer that must be 16-byte aligned is not */
   LBQ_ERR_WORKSPACE = -5,  /* workspace smaller than the *_workspace query returned */
   LBQ_ERR_RANGE = -6,      /* packing: non-finite weight or an RTN group scale out of range */
@@ -96,8 +101,8 @@ typedef enum {
 /* A packed weight: a plain view of caller-owned device buffers. */
 typedef struct {
   int32_t K, N, bits, format;
-  const void *planes;    /* RTN: uint32 [N][K/128][bits][4]; PVQ: uint8 [N][K/4] */
-  const void *meta;      /* RTN: fp16 pairs [N][K/128][2]; PVQ: fp16 [N] */
+  const void *planes;    /* RTN: uint32 [N][K/128][bits][4]; PVQ: uint8 [bits/2][N][K/4] */
+  const void *meta;      /* RTN: fp16 pairs [N][K/128][2]; PVQ: fp16 [bits/2][N] */
   const void *codebook;  /* PVQ: 256x4 e4m3 bytes; RTN: ignored (may be NULL) */
   const int8_t *signs;   /* [K] rotation signs, each +1 or -1 */
 } lbq_weight;
@@ -150,9 +155,10 @@ lbq_status lbq_packed_bytes(int32_t K, int32_t N, int32_t bits, int32_t format,
  * then c), then per group mn = min(0, min w'), mx = max(0, max w'),
  * s = fp16_rne((mx - mn) / (2^b - 1)) (0 -> 1), z = rint(-mn / s),
  * q = clamp(rint(w' / s) + z, 0, 2^b - 1), and scatter q into bit-planes.
- * PVQ (bits 2): rotate, s_n = fp16_rne(rms(w'_n) / rms(C)) (0 -> 1), and per
+ * PVQ (bits 2/4/6): rotate, s_n = fp16_rne(rms(w'_n) / rms(C)) (0 -> 1), and per
  * 4-weight half the nearest codebook entry to w'/s_n (squared distance,
- * ties to the lower index).
+ * ties to the lower index); each further stage does the same on what the
+ * earlier stages left (w' minus their decode), with its own row scale.
  * Returns LBQ_ERR_RANGE for non-finite W, a PVQ scale that overflows fp16, or
  * an RTN scale s >= 128 at 2/3/4 bits or s >= 16 at 8 bits (the MFMA GEMM's
  * decode holds -64 s (-256 s at 8 bits) and -16 s z in fp16; a group would
@@ -208,12 +214,13 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
  *     aligned): one launch, the matrix-core GEMV with the rotation in its
  *     prologue (nothing is written to ws);
  *   - other M <= 4: a rotation launch into ws, then the staged VALU GEMV
- *     (8-bit codes: the MFMA GEMM instead; a forced GEMV that the matrix-core
- *     GEMV cannot take returns LBQ_ERR_SHAPE at 8 bits);
+ *     (8-bit codes and multi-stage PVQ: the MFMA GEMM instead; a forced GEMV
+ *     that the matrix-core GEMV cannot take returns LBQ_ERR_SHAPE for them);
  *   - M >= 5: a rotation launch into ws (folded order, with the RTN
  *     zero-point sums), then the MFMA dequant-GEMM.
  * Accumulation is fp32; the GEMM rounds each decoded RTN weight s q to fp16
- * (the zero-point term s z sum_k x'_k is added separately). The RTN GEMM needs
+ * (the zero-point term s z sum_k x'_k is added separately), and each decoded
+ * multi-stage PVQ weight to one fp16 value in units of stage 1's row scale. The RTN GEMM needs
  * N*K*b/8 < 2^31 - 4096 (LBQ_ERR_SHAPE otherwise). The result of a call does
  * not depend on timing: repeat calls give identical bits. Errors are returned
  * before any launch: LBQ_ERR_NULL, _SHAPE, _BITS, _ALIGN, _FORMAT, _WORKSPACE;
@@ -305,7 +312,7 @@ lbq_status lbq_moe_route(const float *logits, int32_t M, int32_t E, int32_t top_
  * (Qwen3.8-27B Pingala-8 card, "Results": the packed file read back tensor by
  * tensor against freshly regenerated data with zero mismatches): RTN writes
  * uint8 codes [N][K] produced by the kernels' own plane-merge routine; PVQ
- * copies the uint8 indices [N][K/4]. codes: device, 16-byte aligned. */
+ * copies the uint8 indices [bits/2][N][K/4]. codes: device, 16-byte aligned. */
 lbq_status lbq_unpack_codes(const lbq_weight *w, uint8_t *codes, void *stream);
 
 /* out[M][K] (fp16) = R x for each token row, R = blockdiag(c H_128 diag(s))

@@ -409,3 +409,26 @@ def test_split_nibbles_and_readout_errors(L):
     rs = L.lib().lbq_readout_screened
     assert rs(ctypes.byref(r), None, 0, 8, None, None, None, None, 0, None) == 0     # M = 0: no-op
     assert rs(ctypes.byref(r), None, 1, 8, None, None, None, None, 0, None) == -1
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+def test_host_pack_pvq_stages_byte_identical_to_oracle(L, bits):
+    """Residual product-VQ at 4 and 6 bits per weight (2 and 3 stages): the
+    host packer's indices and row scales equal the oracle's, stage by stage."""
+    stages = bits // 2
+    cb = synth.codebook(workload=synth.W_PVQ)
+    assert L.packed_bytes(1024, 10, bits, L.FMT_PVQ_4x8) == (stages * 10 * 256, stages * 10 * 2)
+    for n, k in [(5, 128), (33, 1024)]:
+        w = synth.weights(n, k, workload=8, item=400 + n)
+        s = synth.signs(k, workload=8, item=400 + n)
+        idx, sc = L.pack(w, bits, s, L.FMT_PVQ_4x8, cb)
+        oi, os_ = O.pack_pvq_stages(w, s, cb, stages)
+        assert np.array_equal(idx, oi.reshape(-1))
+        assert np.array_equal(sc, os_.view(np.uint8).reshape(-1))
+
+
+def test_pvq_stage_counts_rejected(L):
+    for bits in (1, 3, 5, 8):
+        with pytest.raises(L.LbqError) as e:
+            L.packed_bytes(128, 4, bits, L.FMT_PVQ_4x8)
+        assert e.value.status == -3
