@@ -96,6 +96,9 @@ KERNEL_SOURCES = {
                         "bit_weight_only_amd/csrc/device.h"],
     "moe_mx_kernel": ["bit_weight_only_amd/csrc/moe_mx.hip", "bit_weight_only_amd/csrc/mx_core.h",
                       "bit_weight_only_amd/csrc/gemm_common.h", "bit_weight_only_amd/csrc/device.h"],
+    "gemm_rtn_grouped_kernel": ["bit_weight_only_amd/csrc/gemm_rtn.hip", "bit_weight_only_amd/csrc/gemm_common.h",
+                                "bit_weight_only_amd/csrc/device.h"],
+    "select_kernel": ["bit_weight_only_amd/csrc/readout.hip", "bit_weight_only_amd/csrc/device.h"],
 }
 
 

@@ -8,9 +8,10 @@
 // (z - 7.5) / 16 put each high nibble at the middle of its 16 codes). This
 // file holds the other two steps:
 //  * top-`cand` rows per token by coarse logit (larger first, ties to the
-//    lower row): a radix select on the fp16 logits' 16-bit order keys, one
-//    workgroup per (token, chunk of 16384 positions), repeated on the chunks'
-//    survivors until one chunk is left;
+//    lower row): a threshold search on the fp16 logits' 16-bit order keys,
+//    two bits per round, one workgroup per
+//    (token, chunk of 4096 positions), repeated on the chunks' survivors
+//    until one chunk is left;
 //  * the exact logits of the survivors from both nibbles, q = lo + 16 hi, with
 //    the 8-bit (s, z): one wavefront per (token, survivor).
 #include "device.h"
@@ -20,7 +21,7 @@ namespace lbq {
 
 namespace {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 256;
 constexpr int kSelPer = 16;
 constexpr int kSelChunk = kSelThreads * kSelPer;   // positions per workgroup
 
@@ -34,9 +35,6 @@ __device__ __forceinline__ uint32_t order16(uint32_t h) {
 // among equal keys the lower row is larger. 0 marks an empty slot.
 __device__ __forceinline__ uint64_t make_key(uint32_t k16, uint32_t row) {
   return (static_cast<uint64_t>(k16 + 1) << 32) | (0xFFFFFFFFu - row);
-}
-__device__ __forceinline__ uint32_t key_value(uint64_t k) {
-  return static_cast<uint32_t>(k >> 32) - 1;
 }
 
 // Bitonic sort of 64 keys, one per lane, into descending order across the wave.
@@ -58,22 +56,26 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
   return v;
 }
 
-// One radix-select step. Stage 1 (keys_in == nullptr) reads fp16 logits
+// One selection step. Stage 1 (keys_in == nullptr) reads fp16 logits
 // vals[M][n] (position = row); later stages read the survivors of the previous
 // one, keys_in[M][n] (each chunk's list sorted, chunks in row order, so
 // position order is row order among equal values). Writes the chunk's `cand`
 // best, sorted, to keys_out[M][gridDim.x][cand] (0 where fewer exist).
+// Thread tid holds positions i * 256 + tid (i < 16) of the chunk.
 __global__ void __launch_bounds__(kSelThreads) select_kernel(const uint16_t *__restrict__ vals,
                                                              const uint64_t *__restrict__ keys_in, int n, int cand,
                                                              uint64_t *__restrict__ keys_out) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wave_cnt[kSelThreads / 64];
-  __shared__ uint32_t sh_b, sh_above, sh_cnt_gt, sh_base;
+  constexpr int W = kSelThreads / 64;
+  static_assert(kSelPer * W == 64, "one scan entry per lane");
+  __shared__ uint32_t cnt[2][W][2];          // per-wave counts of a search round (two rounds in flight)
+  __shared__ uint32_t eq_base[kSelPer * W];  // equal-key counts per (step, wave), then their prefix
+  __shared__ uint32_t sh_cnt_gt;
   __shared__ uint64_t sel[64];
   const int t = blockIdx.y, chunk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   uint64_t key[kSelPer];
+  uint32_t val[kSelPer];   // order key of each held position (0 for empty: every real key is above it)
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
     const long p = static_cast<long>(chunk) * kSelChunk + i * kSelThreads + tid;
@@ -83,112 +85,106 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const uint16_t *__r
       else k = make_key(order16(vals[static_cast<size_t>(t) * n + p]), static_cast<uint32_t>(p));
     }
     key[i] = k;
+    val[i] = static_cast<uint32_t>(k >> 32);   // order key + 1, or 0
   }
   if (tid < 64) sel[tid] = 0;
+  if (tid == 0) sh_cnt_gt = 0;
 
-  // two histogram passes: high byte, then low byte within the chosen high byte
-  uint32_t T = 0, above = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+  // The threshold X: the largest 16-bit order key that at least cand keys
+  // reach, two bits per round from the top (the count of keys >= v falls as v
+  // grows). Each round counts four thresholds in VALU registers (two per
+  // 32-bit word: a thread holds at most 16 keys, a workgroup at most 4096),
+  // adds them across the wave with xor shuffles and across the waves through
+  // LDS, one barrier per round. Fewer than cand keys in all: no threshold,
+  // every key survives. (val = order key + 1, 0 for empty slots.)
+  int buf = 0;
+  auto round_counts = [&](uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t out[4]) {
+    uint32_t p01 = 0, p23 = 0;
 #pragma unroll
     for (int i = 0; i < kSelPer; ++i) {
-      if (key[i] == 0) continue;
-      const uint32_t v = key_value(key[i]);
-      if (pass == 0) atomicAdd(&hist[v >> 8], 1u);
-      else if ((v >> 8) == (T >> 8)) atomicAdd(&hist[v & 255u], 1u);
+      p01 += (val[i] >= c0 ? 1u : 0u) + (val[i] >= c1 ? 0x10000u : 0u);
+      p23 += (val[i] >= c2 ? 1u : 0u) + (val[i] >= c3 ? 0x10000u : 0u);
     }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l holds bins 255 - 4l .. 252 - 4l (descending); counts from the top
-      uint32_t c[4], s = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - 4 * lane - j];
-        s += c[j];
-      }
-      uint32_t incl = s;   // inclusive prefix over lanes
+    for (int d = 32; d > 0; d >>= 1) {
+      p01 += __shfl_xor(p01, d, 64);
+      p23 += __shfl_xor(p23, d, 64);
+    }
+    if (lane == 0) {
+      cnt[buf][wave][0] = p01;
+      cnt[buf][wave][1] = p23;
+    }
+    __syncthreads();   // (a wave writes this buffer again only after the next round's barrier)
+    uint32_t s01 = 0, s23 = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      s01 += cnt[buf][w][0];
+      s23 += cnt[buf][w][1];
+    }
+    out[0] = s01 & 0xFFFFu;
+    out[1] = s01 >> 16;
+    out[2] = s23 & 0xFFFFu;
+    out[3] = s23 >> 16;
+    buf ^= 1;
+  };
+  const uint32_t c = static_cast<uint32_t>(cand);
+  uint32_t tot[4];
+  // first round: every valid key, and the top two bits
+  round_counts(1, (1u << 14) + 1, (2u << 14) + 1, (3u << 14) + 1, tot);
+  const bool all = tot[0] < c;
+  uint32_t X = 0;
+  if (!all) {
+    X = tot[3] >= c ? 3u << 14 : tot[2] >= c ? 2u << 14 : tot[1] >= c ? 1u << 14 : 0u;
+#pragma unroll 1
+    for (int b = 12; b >= 0; b -= 2) {
+      const uint32_t step = 1u << b;
+      round_counts(X + step + 1, X + 2 * step + 1, X + 3 * step + 1, X + 3 * step + 1, tot);
+      X += tot[2] >= c ? 3 * step : tot[1] >= c ? 2 * step : tot[0] >= c ? step : 0;
+    }
+  }
+  const uint32_t T = X + 1;   // the threshold in val units
+
+  // keys above the threshold (at most cand - 1 of them; every key when there
+  // is none), then the lowest positions equal to it, in position order
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    if (val[i] != 0 && (all || val[i] > T)) {
+      const uint32_t slot = atomicAdd(&sh_cnt_gt, 1u);
+      if (slot < 64) sel[slot] = key[i];
+    }
+  }
+  uint64_t bal[kSelPer];
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    bal[i] = all ? 0ull : __ballot(val[i] == T);
+    if (lane == 0) eq_base[i * W + wave] = static_cast<uint32_t>(__popcll(bal[i]));
+  }
+  __syncthreads();
+  if (!all) {
+    const uint32_t g = sh_cnt_gt;
+    const uint32_t need = c - g;
+    // exclusive prefix of the (step, wave) counts in that order: lane l holds entry l
+    uint32_t own = 0;
+    if (wave == 0) {
+      own = eq_base[lane];
+      uint32_t incl = own;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
         const uint32_t o = __shfl_up(incl, d, 64);
         if (lane >= d) incl += o;
       }
-      uint32_t run = above + incl - s;   // keys above this lane's first bin
-      int found = -1;
-      uint32_t found_above = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (found < 0 && run + c[j] >= static_cast<uint32_t>(cand)) {
-          found = 255 - 4 * lane - j;
-          found_above = run;
-        }
-        run += c[j];
-      }
-      const uint64_t hit = __ballot(found >= 0);
-      if (hit == 0) {
-        // fewer than cand keys in all: take everything (threshold below every key)
-        if (lane == 0) {
-          sh_b = 0xFFFFFFFFu;
-          sh_above = above + __shfl(incl, 63, 64);
-        }
-      } else {
-        const int first = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-        const int b = __shfl(found, first, 64);
-        const uint32_t ab = __shfl(found_above, first, 64);
-        if (lane == 0) {
-          sh_b = static_cast<uint32_t>(b);
-          sh_above = ab;
-        }
-      }
+      own = incl - own;
     }
     __syncthreads();
-    if (sh_b == 0xFFFFFFFFu) {   // take all: no threshold
-      T = 0xFFFFFFFFu;
-      above = sh_above;
-      break;
-    }
-    T = pass == 0 ? (sh_b << 8) : ((T & 0xFF00u) | sh_b);
-    above = sh_above;
+    if (wave == 0) eq_base[lane] = own;
     __syncthreads();
-  }
-
-  // keys above the threshold (at most cand - 1 of them; all when T is "none"),
-  // then the lowest positions equal to it, in position order
-  if (tid == 0) {
-    sh_cnt_gt = 0;
-    sh_base = 0;
-  }
-  __syncthreads();
-  const bool all = T == 0xFFFFFFFFu;
-#pragma unroll
-  for (int i = 0; i < kSelPer; ++i) {
-    if (key[i] != 0 && (all || key_value(key[i]) > T)) {
-      const uint32_t slot = atomicAdd(&sh_cnt_gt, 1u);
-      if (slot < 64) sel[slot] = key[i];
-    }
-  }
-  __syncthreads();
-  if (!all) {
-    const uint32_t g = sh_cnt_gt;
-    const uint32_t need = static_cast<uint32_t>(cand) - g;
+    const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int i = 0; i < kSelPer; ++i) {
-      // (sh_base is uniform: once it reaches need, no later key is taken)
-      const bool eq = sh_base < need && key[i] != 0 && key_value(key[i]) == T;
-      const uint64_t b = __ballot(eq);
-      if (lane == 0) wave_cnt[wave] = static_cast<uint32_t>(__popcll(b));
-      __syncthreads();
-      uint32_t before = sh_base;
-      for (int w = 0; w < wave; ++w) before += wave_cnt[w];
-      before += static_cast<uint32_t>(__popcll(b & ((1ull << lane) - 1ull)));
-      if (eq && before < need) sel[g + before] = key[i];
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t tot = 0;
-        for (int w = 0; w < kSelThreads / 64; ++w) tot += wave_cnt[w];
-        sh_base += tot;
+      if ((bal[i] >> lane) & 1ull) {
+        const uint32_t r = eq_base[i * W + wave] + static_cast<uint32_t>(__popcll(bal[i] & below));
+        if (r < need) sel[g + r] = key[i];
       }
-      __syncthreads();
     }
   }
   __syncthreads();
@@ -200,8 +196,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const uint16_t *__r
 
 // Exact logits of the survivors: wavefront (t, c) scores row r = the row of
 // keys[t][c] from both nibble plane sets and the 8-bit (s, z), against the
-// rotated activations xr [M][K] fp16. Lane l takes codes 2l, 2l + 1 of every
-// group (word l / 16, bits 2 (l mod 16) and the next).
+// rotated activations xr [M][K] fp16. Per pass of 16 groups, lane l takes word
+// column l mod 4 (32 consecutive codes) of group l / 4: its eight plane words,
+// the group's (s, z) and 64 bytes of x' are all loaded before any use, so a
+// pass costs one memory round trip.
 __global__ void __launch_bounds__(256) refine_kernel(const uint64_t *__restrict__ keys, const uint32_t *__restrict__ hi,
                                                      const uint32_t *__restrict__ lo, const uint32_t *__restrict__ meta,
                                                      const uint16_t *__restrict__ xr, int M, int K, int N, int cand,
@@ -221,28 +219,42 @@ __global__ void __launch_bounds__(256) refine_kernel(const uint64_t *__restrict_
   }
   const int row = static_cast<int>(rk);
   const int G = K / kGroup;
-  const int w = lane >> 4, j = 2 * (lane & 15);
-  const uint32_t *hr = hi + static_cast<size_t>(row) * G * 16;
-  const uint32_t *lr = lo + static_cast<size_t>(row) * G * 16;
-  const uint32_t *mr = meta + static_cast<size_t>(row) * G;
-  const uint32_t *xp = reinterpret_cast<const uint32_t *>(xr + static_cast<size_t>(t) * K) + lane;
+  const int w = lane & 3;
   float acc = 0.0f;
-  for (int g = 0; g < G; ++g) {
-    uint32_t q0 = 0, q1 = 0;
+  for (int g0 = 0; g0 < G; g0 += 16) {
+    const int g = g0 + (lane >> 2);
+    if (g < G) {
+      const size_t gi = static_cast<size_t>(row) * G + g;
+      uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lw = lr[g * 16 + p * 4 + w] >> j;
-      const uint32_t hw = hr[g * 16 + p * 4 + w] >> j;
-      q0 |= ((lw & 1u) | ((hw & 1u) << 4)) << p;
-      q1 |= (((lw >> 1) & 1u) | (((hw >> 1) & 1u) << 4)) << p;
+      for (int p = 0; p < 4; ++p) {
+        hw[p] = hi[gi * 16 + p * 4 + w];
+        lw[p] = lo[gi * 16 + p * 4 + w];
+      }
+      const uint32_t m = meta[gi];
+      const uint4 *xp = reinterpret_cast<const uint4 *>(xr + static_cast<size_t>(t) * K + g * kGroup + 32 * w);
+      uint4 xv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xv[v] = xp[v];
+      const float s = f16_bits_to_f32(m & 0xFFFFu);
+      const float z = f16_bits_to_f32(m >> 16);
+      float dot = 0.0f, xs = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t pair[4] = {xv[v].x, xv[v].y, xv[v].z, xv[v].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 8 * v + e;   // code 32 w + j
+          uint32_t q = 0;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) q |= (((lw[p] >> j) & 1u) << p) | (((hw[p] >> j) & 1u) << (p + 4));
+          const float x = f16_bits_to_f32((pair[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          dot += static_cast<float>(q) * x;
+          xs += x;
+        }
+      }
+      acc += s * (dot - z * xs);
     }
-    const uint32_t m = mr[g];
-    const float s = f16_bits_to_f32(static_cast<uint16_t>(m & 0xFFFFu));
-    const float z = f16_bits_to_f32(static_cast<uint16_t>(m >> 16));
-    const uint32_t xv = xp[g * 64];
-    const float x0 = f16_bits_to_f32(static_cast<uint16_t>(xv & 0xFFFFu));
-    const float x1 = f16_bits_to_f32(static_cast<uint16_t>(xv >> 16));
-    acc += s * ((static_cast<float>(q0) - z) * x0 + (static_cast<float>(q1) - z) * x1);
   }
 #pragma unroll
   for (int d = 32; d > 0; d >>= 1) acc += __shfl_xor(acc, d, 64);
