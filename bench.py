@@ -1034,17 +1034,18 @@ def trace_table(trace_dir, out_path):
         stats += list(csv.DictReader(open(f)))
     lines = [
         "rocprofv3 kernel-trace statistics of the default bench command (all parts of the hot path:",
-        "dense stack at M=1, 4, 16; FFN pair at M=1, 8, 64, 256; product-VQ at M=1, 16, 64; MoE block at M=32;",
-        "oracle timing on the host runs no GPU kernels).",
+        "dense stack at M=1, 4, 16; FFN pair at M=1, 8, 64, 256; product-VQ at M=1, 16, 64 at 2 and 6 bits",
+        "per weight; MoE block at M=32, 256, 2048; the screened 8-bit readout at M=1, 4; the streaming-read",
+        "floor; oracle timing on the host runs no GPU kernels).",
         "",
         "command (run from the repository root, cd /tmp && export TMPDIR=/tmp first):",
         "  rocprofv3 --kernel-trace --stats -d <dir> -o k --output-format csv -- python3 bench.py",
         "  python3 bench.py --trace-summary <dir> <this file>",
         "",
-        f"  {'kernel':100s} {'calls':>7s} {'avg us':>10s} {'min us':>9s} {'total us':>12s}",
+        f"  {'kernel':130s} {'calls':>7s} {'avg us':>10s} {'min us':>9s} {'total us':>12s}",
     ]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append(f"  {r['Name'][:100]:100s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} "
+        lines.append(f"  {r['Name'][:130]:130s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} "
                      f"{float(r['MinNs']) / 1e3:9.3f} {float(r['TotalDurationNs']) / 1e3:12.1f}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -36,7 +36,8 @@ lbq_status check_weight(const lbq_weight *w) {
 }
 
 GemmPlan linear_gemm_plan(const lbq_weight *w, int M) {
-  return w->format == LBQ_FMT_RTN_PLANES ? gemm_rtn_plan(M, w->K, w->N, w->bits) : gemm_plan(M, w->K, w->N);
+  return w->format == LBQ_FMT_RTN_PLANES ? gemm_rtn_plan(M, w->K, w->N, w->bits)
+                                          : gemm_plan(M, w->K, w->N, w->bits / 2);
 }
 
 size_t tz_bytes(const lbq_weight *w, int M) {
@@ -522,8 +523,8 @@ lbq_status lbq_readout_screened(const lbq_readout *r, const uint16_t *x, int32_t
   if (st != LBQ_OK) return st;
   // 2. the survivors per token, 3. their exact logits
   const uint64_t *fin = nullptr;
-  if (launch_rotate(x, M, r->K, r->signs, xr, s) != hipSuccess) return LBQ_ERR_HIP;
-  if (launch_readout_select(coarse, M, r->N, cand, keys, &fin, s) != hipSuccess) return LBQ_ERR_HIP;
+  if (launch_readout_select(coarse, M, r->N, cand, keys, &fin, x, r->signs, xr, r->K, s) != hipSuccess)
+    return LBQ_ERR_HIP;
   return hip_status(launch_readout_refine(fin, r->hi_planes, r->lo_planes, r->meta, xr, M, r->K, r->N, cand, ids,
                                           logits, s));
 }

@@ -333,20 +333,23 @@ void launch_pvq_st(int nb, int mt, dim3 grid, const uint8_t *idx, const uint8_t 
 
 }  // namespace
 
-GemmPlan gemm_plan(int M, int K, int N) {
+GemmPlan gemm_plan(int M, int K, int N, int stages) {
   // Token tiles of 16, 32 or 64. Two row blocks per wave only with >= 512 such
   // tiles, else one; then split K until about 768 workgroups run at up to 16
   // tokens and 384 beyond, every slice keeping at least four groups (measured
-  // on the product-VQ 4096 -> 14336 shape at 16 and 64 tokens).
+  // on the product-VQ 4096 -> 14336 shape at 16 and 64 tokens). Residual
+  // stages carry more index bytes per weight: two row blocks per wave and
+  // half as many workgroups (4096 -> 14336 at three stages: 16 tokens
+  // 32.9 -> 26.6 us, 64 tokens 57.4 -> 44.9 us).
   GemmPlan p;
   p.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   const int G = K / kGroup;
   p.m_tiles = M > 0 ? (M + 16 * p.mt - 1) / (16 * p.mt) : 0;
   const long tiles2 = static_cast<long>((N + 127) / 128) * p.m_tiles;
-  p.nb = tiles2 >= 512 ? 2 : 1;
+  p.nb = (tiles2 >= 512 || stages > 1) ? 2 : 1;
   p.n_tiles = (N + 64 * p.nb - 1) / (64 * p.nb);
   const long tiles = static_cast<long>(p.n_tiles) * p.m_tiles;
-  const long target = M <= 16 ? 768 : 384;
+  const long target = (M <= 16 ? 768 : 384) / (stages > 1 ? 2 : 1);
   p.S = 1;
   while (tiles * p.S < target && p.S < 16) p.S *= 2;
   while (p.S > 1 && p.S * 4 > G) p.S /= 2;

@@ -13,10 +13,12 @@ hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, u
 
 // Screened readout (readout.hip): the survivors' selection by coarse logit
 // (keys: readout_key_bytes of scratch; *final_keys receives the [M][cand]
-// sorted survivors inside it) and their exact logits from the nibble planes.
+// sorted survivors inside it; the first launch also writes xr = R x, fp16
+// [M][K]) and their exact logits from the nibble planes.
 size_t readout_key_bytes(int M, int N, int cand);
 hipError_t launch_readout_select(const uint16_t *coarse, int M, int N, int cand, uint64_t *keys,
-                                 const uint64_t **final_keys, hipStream_t s);
+                                 const uint64_t **final_keys, const uint16_t *x, const int8_t *signs, uint16_t *xr,
+                                 int K, hipStream_t s);
 hipError_t launch_readout_refine(const uint64_t *keys, const void *hi, const void *lo, const void *meta,
                                  const uint16_t *xr, int M, int K, int N, int cand, int32_t *ids, float *logits,
                                  hipStream_t s);
@@ -74,7 +76,7 @@ struct GemmPlan {
   int nb, mt, S, n_tiles, m_tiles;
   int kw = 1;   // RTN GEMM: wave sets per workgroup (2: alternate groups, 512 threads)
 };
-GemmPlan gemm_plan(int M, int K, int N);
+GemmPlan gemm_plan(int M, int K, int N, int stages);
 GemmPlan gemm_rtn_plan(int M, int K, int N, int bits);
 // longest K slice (groups) whose scale/zero words the RTN GEMM stages in LDS,
 // for nb row blocks per wave; launch_gemm_rtn rejects plans with longer slices

@@ -13,8 +13,10 @@
 //    (token, chunk of 4096 positions), repeated on the chunks' survivors
 //    until one chunk is left;
 //  * the exact logits of the survivors from both nibbles, q = lo + 16 hi, with
-//    the 8-bit (s, z): one wavefront per (token, survivor).
+//    the 8-bit (s, z): one wavefront per (token, survivor), against x rotated
+//    to fp16 by extra workgroups of the first selection launch.
 #include "device.h"
+#include "gemv_core.h"
 #include "kernels.h"
 
 namespace lbq {
@@ -60,11 +62,17 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
 // vals[M][n] (position = row); later stages read the survivors of the previous
 // one, keys_in[M][n] (each chunk's list sorted, chunks in row order, so
 // position order is row order among equal values). Writes the chunk's `cand`
-// best, sorted, to keys_out[M][gridDim.x][cand] (0 where fewer exist).
+// best, sorted, to keys_out[M][chunks][cand] (0 where fewer exist).
 // Thread tid holds positions i * 256 + tid (i < 16) of the chunk.
+// Workgroups past the chunks (first stage only) rotate token blockIdx.y for
+// the exact step instead, one 128-group per wavefront: xr = R x, fp32
+// butterflies, fp16 out (a launch of its own would cost more than the work).
 __global__ void __launch_bounds__(kSelThreads) select_kernel(const uint16_t *__restrict__ vals,
                                                              const uint64_t *__restrict__ keys_in, int n, int cand,
-                                                             uint64_t *__restrict__ keys_out) {
+                                                             uint64_t *__restrict__ keys_out, int chunks,
+                                                             const uint32_t *__restrict__ x,
+                                                             const int8_t *__restrict__ signs,
+                                                             uint32_t *__restrict__ xr, int K) {
   constexpr int W = kSelThreads / 64;
   static_assert(kSelPer * W == 64, "one scan entry per lane");
   __shared__ uint32_t cnt[2][W][2];          // per-wave counts of a search round (two rounds in flight)
@@ -73,6 +81,19 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const uint16_t *__r
   __shared__ uint64_t sel[64];
   const int t = blockIdx.y, chunk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (chunk >= chunks) {
+    const int g = (chunk - chunks) * W + wave;
+    if (g >= K / kGroup) return;
+    const long base = static_cast<long>(t) * K + g * kGroup;   // element index
+    const uint32_t xv = x[(base >> 1) + lane];
+    const int k0 = g * kGroup + 2 * lane;
+    float v0 = half_lo(xv) * static_cast<float>(signs[k0]);
+    float v1 = half_hi(xv) * static_cast<float>(signs[k0 + 1]);
+    fwht128_wave(v0, v1, lane);
+    xr[(base >> 1) + lane] = static_cast<uint32_t>(f32_to_f16_bits(v0 * kInvSqrt128)) |
+                             (static_cast<uint32_t>(f32_to_f16_bits(v1 * kInvSqrt128)) << 16);
+    return;
+  }
 
   uint64_t key[kSelPer];
   uint32_t val[kSelPer];   // order key of each held position (0 for empty: every real key is above it)
@@ -190,7 +211,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const uint16_t *__r
   __syncthreads();
   if (wave == 0) {
     const uint64_t v = wave_sort_desc(sel[lane]);
-    if (lane < cand) keys_out[(static_cast<size_t>(t) * gridDim.x + chunk) * cand + lane] = v;
+    if (lane < cand) keys_out[(static_cast<size_t>(t) * chunks + chunk) * cand + lane] = v;
   }
 }
 
@@ -277,20 +298,26 @@ size_t readout_key_bytes(int M, int N, int cand) {
 }
 
 hipError_t launch_readout_select(const uint16_t *coarse, int M, int N, int cand, uint64_t *keys,
-                                 const uint64_t **final_keys, hipStream_t s) {
+                                 const uint64_t **final_keys, const uint16_t *x, const int8_t *signs, uint16_t *xr,
+                                 int K, hipStream_t s) {
   *final_keys = keys;
   if (M <= 0) return hipSuccess;
   if (cand < 1 || cand > 64 || N < 1 || M > 65535) return hipErrorInvalidValue;
   const size_t half = readout_key_bytes(M, N, cand) / 2;
   uint64_t *buf[2] = {keys, reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(keys) + half)};
   int n = N, chunks = readout_chunks(N), b = 0;
-  hipLaunchKernelGGL(select_kernel, dim3(chunks, M), dim3(kSelThreads), 0, s, coarse,
-                     static_cast<const uint64_t *>(nullptr), n, cand, buf[b]);
+  // the first stage also rotates x for the exact step (kSelThreads / 64 groups per extra workgroup)
+  const int rot_wgs = (K / kGroup + kSelThreads / 64 - 1) / (kSelThreads / 64);
+  hipLaunchKernelGGL(select_kernel, dim3(chunks + rot_wgs, M), dim3(kSelThreads), 0, s, coarse,
+                     static_cast<const uint64_t *>(nullptr), n, cand, buf[b], chunks,
+                     reinterpret_cast<const uint32_t *>(x), signs, reinterpret_cast<uint32_t *>(xr), K);
   while (chunks > 1) {
     n = chunks * cand;
     chunks = readout_chunks(n);
     hipLaunchKernelGGL(select_kernel, dim3(chunks, M), dim3(kSelThreads), 0, s,
-                       static_cast<const uint16_t *>(nullptr), buf[b], n, cand, buf[b ^ 1]);
+                       static_cast<const uint16_t *>(nullptr), buf[b], n, cand, buf[b ^ 1], chunks,
+                       static_cast<const uint32_t *>(nullptr), static_cast<const int8_t *>(nullptr),
+                       static_cast<uint32_t *>(nullptr), K);
     b ^= 1;
   }
   *final_keys = buf[b];   // [M][cand], sorted per token
