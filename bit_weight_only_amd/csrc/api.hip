@@ -99,9 +99,12 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
     uint8_t *after_x = static_cast<uint8_t *>(ws) + round_up(static_cast<size_t>(M) * w->K * 2, kAlign);
     uint32_t *tz = rtn ? reinterpret_cast<uint32_t *>(after_x) : nullptr;
     void *scratch = after_x + tz_bytes(w, M);
-    if (launch_rotate_folded(x, M, w->K, w->signs, xr, tz, gemm_counter_ptr(gp, scratch), gemm_counters(gp), s,
-                             rot_tokens) != hipSuccess)
-      return LBQ_ERR_HIP;
+    // (the RTN GEMM takes the folded slot order, the product-VQ GEMM natural order)
+    const hipError_t re =
+        rtn ? launch_rotate_folded(x, M, w->K, w->signs, xr, tz, gemm_counter_ptr(gp, scratch), gemm_counters(gp), s,
+                                   rot_tokens)
+            : launch_rotate_clear(x, M, w->K, w->signs, xr, gemm_counter_ptr(gp, scratch), gemm_counters(gp), s);
+    if (re != hipSuccess) return LBQ_ERR_HIP;
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return LBQ_ERR_HIP;
     const hipError_t ge =
         rtn ? launch_gemm_rtn(gp, w->bits, w->planes, w->meta, xr, tz, y, M, w->K, w->N, scratch, s)

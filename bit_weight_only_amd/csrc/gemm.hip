@@ -7,17 +7,18 @@
 // and 16 * MT tokens; wave w owns NB blocks of 16 rows. The K range of the
 // workgroup is one of S contiguous slices of the 128-groups (split-K when the
 // tile grid alone would leave the chip idle). Per group:
-//   * the token tile's rotated activations (folded slot order: slot c of a
-//     32-chunk = (x[c], x[c+16])) and the wave's index bytes are copied
-//     global -> LDS asynchronously (global_load_lds) into a ring of R slots,
-//     R - 1 groups ahead of the contraction, one barrier per group;
+//   * the token tile's rotated activations (natural order) and the wave's
+//     index bytes are copied global -> LDS asynchronously (global_load_lds)
+//     into a ring of R slots, R - 1 groups ahead of the contraction, one
+//     barrier per group;
 //   * lane (j, kq) of a wave looks up the codebook entries of word column kq
-//     of row j of each of its NB row blocks (e4m3 values are exact in fp16,
-//     staged as a 2 KB fp16 table in LDS): 16 slots, the B operands of the
-//     group's 4 k-steps (slots 4t..4t+3 for step t). The A operand of lane
-//     (i, kq) is slots 4t..4t+3 of token i's chunk kq, so A and B agree on
-//     which k each element is. The row scale is constant along K and applied
-//     once at the end.
+//     (weights 32 kq .. 32 kq + 31) of row j of each of its NB row blocks
+//     (e4m3 values are exact in fp16, staged as a 2 KB fp16 table in LDS):
+//     step t takes weights 32 kq + 8 t .. + 7, the two entries of index bytes
+//     8 kq + 2 t and the next, whose four fp16 values each are already the
+//     B operand's pairs. The A operand of lane (i, kq) is x[32 kq + 8 t .. + 7]
+//     of token i, so A and B agree on which k each element is. The row scale
+//     is constant along K and applied once at the end.
 // Split-K: each workgroup writes its fp32 partial tile to the workspace; the
 // last of the S workgroups of a tile to arrive (an atomic counter the rotation
 // launch cleared) sums the S partials in slice order and writes y, so the
@@ -86,8 +87,9 @@ struct PvqTile {
                       bslot + kBVecs * (kWaves * st + wave) + 64 * t);
       }
   }
-  // slot c = (w[c], w[c+16]); weights 4t..4t+3 use index byte t, weights
-  // 16+4t.. use index byte t+4.
+  // Natural order: the fp16 pairs of k-step t are weights 8 t .. 8 t + 7 of the
+  // lane's word column, i.e. the two codebook entries of index bytes 2 t and
+  // 2 t + 1 as they stand (four fp16 values each, no repacking).
   __device__ __forceinline__ void decode(const uint4 *bslot, int wave, int lane, uint32_t b[NB][16]) const {
     const int j = lane & 15, kq = lane >> 4;
 #pragma unroll
@@ -99,12 +101,12 @@ struct PvqTile {
                                                          (u & 3) * 16 + j)[kq & 1];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint32_t ia = (w.x >> (8 * t)) & 0xFFu;
-          const uint32_t ib = (w.y >> (8 * t)) & 0xFFu;
+          const uint32_t word = t < 2 ? w.x : w.y;
+          const uint32_t ia = (word >> (16 * (t & 1))) & 0xFFu;
+          const uint32_t ib = (word >> (16 * (t & 1) + 8)) & 0xFFu;
           const uint2 ca = *reinterpret_cast<const uint2 *>(lut + 2 * ia);
           const uint2 cb = *reinterpret_cast<const uint2 *>(lut + 2 * ib);
-          const uint32_t v[4] = {(ca.x & 0xFFFFu) | (cb.x << 16), (ca.x >> 16) | (cb.x & 0xFFFF0000u),
-                                 (ca.y & 0xFFFFu) | (cb.y << 16), (ca.y >> 16) | (cb.y & 0xFFFF0000u)};
+          const uint32_t v[4] = {ca.x, ca.y, cb.x, cb.y};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if (st == 0) {

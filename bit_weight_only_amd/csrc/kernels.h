@@ -10,6 +10,9 @@
 namespace lbq {
 
 hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, hipStream_t s);
+// the same, clearing n_counters u32 counters first (the PVQ GEMM's split-K arrivals)
+hipError_t launch_rotate_clear(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out,
+                               uint32_t *counters, int n_counters, hipStream_t s);
 
 // Screened readout (readout.hip): the survivors' selection by coarse logit
 // (keys: readout_key_bytes of scratch; *final_keys receives the [M][cand]

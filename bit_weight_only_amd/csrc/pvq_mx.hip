@@ -61,21 +61,20 @@ __device__ __forceinline__ void rot_pieces_pvq(const RotIn &in, int Gp, int m, i
 }
 
 // x: raw activations [M][K] fp16 (M <= 4); signs: [K] int8 (+-1), 16-byte aligned.
-template <int DEPTH>
+template <int DEPTH, int ST>
 __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4 *__restrict__ idx,
                                                                   const uint16_t *__restrict__ row_scale,
                                                                   const uint32_t *__restrict__ codebook,
                                                                   const uint4 *__restrict__ x,
                                                                   const uint4 *__restrict__ signs,
-                                                                  uint16_t *__restrict__ y, const MxShape sh,
-                                                                  const int stages_arg) {
+                                                                  uint16_t *__restrict__ y, const MxShape sh) {
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   const int M = sh.M, K = sh.K, N = sh.N, G = sh.G, Gp = sh.Gp;
   const int VR = G * 2;                          // 16-byte index vectors per row
   const int b = static_cast<int>(blockIdx.x);
   const int ntl = sh.tq + (b < sh.tr ? 1 : 0);   // this workgroup's tiles: b + k grid, k < ntl
   const int rows = ntl * 16;
-  const int stages = stages_arg;
+  constexpr int stages = ST;
   const int vrows = stages * rows;               // partial-sum rows: stage-major virtual tiles
   const int items = stages * ntl * sh.NB;
   const int nw = static_cast<int>(blockDim.x >> 6), nt = static_cast<int>(blockDim.x);
@@ -108,9 +107,11 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
   auto load = [&](uint4 &it) {
     const uint32_t past = lc.i < items ? 0u : kOutOfRange;
     int st = 0, tl = lc.tile;   // virtual tile -> (stage, tile)
-    while (tl >= ntl && st + 1 < stages) {
-      tl -= ntl;
-      ++st;
+#pragma unroll
+    for (int k2 = 1; k2 < stages; ++k2) {
+      const bool next = tl >= ntl;
+      tl -= next ? ntl : 0;
+      st += next ? 1 : 0;
     }
     const uint32_t pstep =
         static_cast<uint32_t>((tl * tstride * VR + lc.batch * kGB * 2) * 16 + st * N * VR * 16) + past;
@@ -284,7 +285,7 @@ hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, con
   const int block = pvq_mx_block(N);
   const MxShape sh = make_shape(M, K, N, 2, grid, block);   // batches of two groups
   const size_t lds = pvq_mx_lds(M, sh.G, (sh.tq + (sh.tr ? 1 : 0)) * 16, block, stages);
-  auto kern = gemv_pvq_mx_kernel<2>;
+  auto kern = stages == 1 ? gemv_pvq_mx_kernel<2, 1> : stages == 2 ? gemv_pvq_mx_kernel<2, 2> : gemv_pvq_mx_kernel<2, 3>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -292,7 +293,7 @@ hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, con
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(block), lds, s, reinterpret_cast<const uint4 *>(idx), row_scale,
                      reinterpret_cast<const uint32_t *>(codebook), reinterpret_cast<const uint4 *>(x),
-                     reinterpret_cast<const uint4 *>(signs), y, sh, stages);
+                     reinterpret_cast<const uint4 *>(signs), y, sh);
   return hipGetLastError();
 }
 

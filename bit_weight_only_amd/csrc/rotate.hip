@@ -14,8 +14,14 @@
 
 namespace lbq {
 
+// Natural-order rotation, one 128-block per wavefront (two values per lane);
+// workgroup 0 also clears n_counters u32 counters (a product-VQ GEMM's split-K
+// arrival counters) ahead of the GEMM launch that uses them.
 __global__ void __launch_bounds__(256) rotate_kernel(const uint32_t *__restrict__ x, const int8_t *__restrict__ signs,
-                                                     uint32_t *__restrict__ out, int M, int K) {
+                                                     uint32_t *__restrict__ out, int M, int K,
+                                                     uint32_t *__restrict__ counters, int n_counters) {
+  if (blockIdx.x == 0)
+    for (int i = static_cast<int>(threadIdx.x); i < n_counters; i += 256) counters[i] = 0;
   const int lane = threadIdx.x & 63;
   const int blocks_per_row = K / kGroup;
   const long blk = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -212,13 +218,18 @@ hipError_t launch_rotate_folded(const uint16_t *x, int M, int K, const int8_t *s
   return hipGetLastError();
 }
 
-hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, hipStream_t s) {
+hipError_t launch_rotate_clear(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out,
+                               uint32_t *counters, int n_counters, hipStream_t s) {
   const long nblk = static_cast<long>(M) * (K / kGroup);
   if (nblk == 0) return hipSuccess;
   const unsigned grid = static_cast<unsigned>((nblk + 3) / 4);
   hipLaunchKernelGGL(rotate_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<const uint32_t *>(x), signs,
-                     reinterpret_cast<uint32_t *>(out), M, K);
+                     reinterpret_cast<uint32_t *>(out), M, K, counters, n_counters);
   return hipGetLastError();
+}
+
+hipError_t launch_rotate(const uint16_t *x, int M, int K, const int8_t *signs, uint16_t *out, hipStream_t s) {
+  return launch_rotate_clear(x, M, K, signs, out, nullptr, 0, s);
 }
 
 }  // namespace lbq
