@@ -129,8 +129,9 @@ def stats(vals, scale=1.0, nd=3):
 
 
 def gpu_clocks():
-    """Current shader / memory clock levels of the first GPU as the driver
-    reports them (sysfs dpm tables; the line marked '*' is current)."""
+    """Current shader / memory clock levels of the first GPU as the amdgpu
+    kernel module reports them (sysfs dpm tables; the line marked '*' is
+    current)."""
     out = {}
     for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))[:1]:
         d = os.path.dirname(f)
