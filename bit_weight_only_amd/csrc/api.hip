@@ -91,8 +91,8 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
     gemv = false;
   }
   if (!gemv) {
-    // MFMA GEMM: rotation into the folded order (with the RTN zero-point sums,
-    // clearing the split-K counters), then the GEMM
+    // MFMA GEMM: a rotation launch (clearing the split-K counters; for RTN the
+    // folded order with the zero-point sums), then the GEMM
     const bool rtn = w->format == LBQ_FMT_RTN_PLANES;
     if (rtn && !gemm_rtn_supported(w->K, w->N, w->bits)) return LBQ_ERR_SHAPE;
     const GemmPlan gp = linear_gemm_plan(w, M);

@@ -126,7 +126,7 @@ struct PvqTile {
 // ------------------------------------------------------------------ mainloop
 
 struct GemmArgs {
-  const uint4 *xf;            // rotated activations [M][K], folded slot order
+  const uint4 *xf;            // rotated activations [M][K], natural order
   uint16_t *y;                // [M][N]
   float *part;                // split-K partial tiles (S > 1)
   uint32_t *counters;         // split-K arrival counters, one per tile, zero on entry

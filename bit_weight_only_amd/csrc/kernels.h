@@ -68,9 +68,10 @@ bool gemv_pvq_mx_supported(int M, int K, int N, int stages);
 hipError_t launch_gemv_pvq_mx(const uint8_t *idx, const uint16_t *row_scale, const uint8_t *codebook,
                               const uint16_t *x, const int8_t *signs, uint16_t *y, int M, int K, int N, int stages,
                               hipStream_t s);
-// MFMA dequant-GEMMs on activations rotated into the folded slot order
-// (launch_rotate_folded): RTN planes (gemm_rtn_plan, launch_gemm_rtn, with the
-// rotation's tz sums) and product-VQ (gemm_plan, launch_gemm_pvq). A plan fixes
+// MFMA dequant-GEMMs: RTN planes on activations rotated into the folded slot
+// order (launch_rotate_folded; gemm_rtn_plan, launch_gemm_rtn, with the
+// rotation's tz sums) and product-VQ on activations in natural order
+// (launch_rotate_clear; gemm_plan, launch_gemm_pvq). A plan fixes
 // the tiling (nb row blocks of 16 per wave, mt token tiles of 16) and the
 // split-K count; split-K needs gemm_scratch_bytes(plan) of scratch whose
 // arrival counters (gemm_counter_ptr, gemm_counters of them) are zero when the

@@ -216,8 +216,8 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
  *   - other M <= 4: a rotation launch into ws, then the staged VALU GEMV
  *     (8-bit codes and multi-stage PVQ: the MFMA GEMM instead; a forced GEMV
  *     that the matrix-core GEMV cannot take returns LBQ_ERR_SHAPE for them);
- *   - M >= 5: a rotation launch into ws (folded order, with the RTN
- *     zero-point sums), then the MFMA dequant-GEMM.
+ *   - M >= 5: a rotation launch into ws (for RTN in the GEMM's folded
+ *     order, with the zero-point sums), then the MFMA dequant-GEMM.
  * Accumulation is fp32; the GEMM rounds each decoded RTN weight s q to fp16
  * (the zero-point term s z sum_k x'_k is added separately), and each decoded
  * multi-stage PVQ weight to one fp16 value in units of stage 1's row scale. The RTN GEMM needs

@@ -31,7 +31,7 @@ def _both(L, pl, x):
     return a, b
 
 
-@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("bits", [2, 3, 8])
 def test_noalloc_matches_workspace_entry_point(L, dev, bits):
     """GEMM with split-K (partials and arrival counters in the scratch) at 64
     tokens, then a smaller call at 9 tokens (fewer tiles, the counters cleared
@@ -55,6 +55,24 @@ def test_noalloc_pvq_gemm(L, dev):
         a, b = _both(L, pl, to_dev(x16, dev))
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), m
         assert O.rel_l2(b.astype(np.float64), oracle_pvq_rows(w, s, cb, x16)) < TOL
+
+
+def test_noalloc_pvq_three_stages(L, dev):
+    """6 bits per weight (three residual stages): the GEMM at 40 then 17
+    tokens and the matrix-core GEMV at 3, identical bits to the workspace call."""
+    n, k = 384, 1024
+    cb = synth.codebook(workload=30)
+    w = synth.weights(n, k, workload=30, item=8)
+    s = synth.signs(k, workload=30, item=8)
+    idx, sc = L.pack(w, 6, s, L.FMT_PVQ_4x8, cb)
+    pl = L.PackedLinear.from_host(idx, sc, s, k, n, 6, L.FMT_PVQ_4x8, cb)
+    for m in (40, 17, 3):
+        say(f"noalloc pvq 6 bpw m={m}")
+        x16 = synth.activations(m, k, workload=30, item=200 + m)
+        a, b = _both(L, pl, to_dev(x16, dev))
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), m
+        oi, os_ = O.pack_pvq_stages(w, s, cb, 3)
+        assert O.rel_l2(b.astype(np.float64), O.linear_pvq_stages(x16, oi, os_, cb, s)) < TOL
 
 
 def test_noalloc_rejects_oversized_calls(L, dev):
