@@ -152,8 +152,11 @@ struct Ring {
   uint4 *b[R];
 };
 
-template <int NB, int ST, int MT, int R>
-__device__ __forceinline__ void gemm_body(const PvqTile<NB, ST> &tile, const GemmArgs &a, const Ring<R> &ring) {
+// pre() runs once the first R - 1 groups' copies are in flight (it fills the
+// codebook table and passes a barrier).
+template <int NB, int ST, int MT, int R, class Pre>
+__device__ __forceinline__ void gemm_body(const PvqTile<NB, ST> &tile, const GemmArgs &a, const Ring<R> &ring,
+                                          Pre pre) {
   constexpr int CA = MT;   // activation copies per wave per group
   const int G = a.K / kGroup;
   const int lane = threadIdx.x & 63;
@@ -214,6 +217,7 @@ __device__ __forceinline__ void gemm_body(const PvqTile<NB, ST> &tile, const Gem
 
 #pragma unroll
   for (int q = 0; q < R - 1; ++q) request(q, g0 + q);
+  pre();
   for (int g = g0; g < g1; g += R) {
 #pragma unroll
     for (int q = 0; q < R; ++q) {
@@ -303,18 +307,27 @@ __global__ void __launch_bounds__(kThreads) gemm_pvq_kernel(const uint8_t *__res
     }
   }
   __shared__ __attribute__((aligned(16))) uint32_t lut[512];
-  // e4m3 -> fp16 table: 256 entries x 4 values, 2 u32 per entry.
-  for (int e = threadIdx.x; e < 512; e += kThreads) {
-    const uint32_t two = reinterpret_cast<const uint16_t *>(codebook)[e];
-    uint32_t out = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) out |= static_cast<uint32_t>(e4m3_to_f16_bits((two >> (8 * h)) & 0xFFu)) << (16 * h);
-    lut[e] = out;
-  }
-  __syncthreads();
+  // e4m3 -> fp16 table: 256 entries x 4 values, 2 u32 per entry. The codebook
+  // words are loaded first and written to LDS once the ring's first copies are
+  // in flight, so the two round trips overlap.
+  static_assert(2 * kThreads == 512, "two table words per thread");
+  const uint16_t *cb16 = reinterpret_cast<const uint16_t *>(codebook);
+  const uint32_t two0 = cb16[threadIdx.x], two1 = cb16[threadIdx.x + kThreads];
   Tile tile{idx, lut, a.K, a.N, {}};
   tile.prepare(a.row_scale, blockIdx.y * (kWaves * 16 * NB) + (threadIdx.x >> 6) * 16 * NB + (threadIdx.x & 15));
-  gemm_body<NB, ST, MT, R>(tile, a, ring);
+  auto fill_lut = [&]() {
+    const uint32_t two[2] = {two0, two1};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      uint32_t out = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        out |= static_cast<uint32_t>(e4m3_to_f16_bits((two[i] >> (8 * h)) & 0xFFu)) << (16 * h);
+      lut[threadIdx.x + i * kThreads] = out;
+    }
+    barrier_lds();   // the table is complete; the ring's copies stay in flight
+  };
+  gemm_body<NB, ST, MT, R>(tile, a, ring, fill_lut);
 }
 
 template <int NB, int ST>

@@ -48,6 +48,19 @@ __device__ __forceinline__ void wait_vm_lds() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also waits
+// for every global load the wave has in flight (its fence covers global memory),
+// which drains a prefetch ring at the barrier; here only this wave's LDS
+// operations complete first (the fences name the local address space), and the
+// ring's loads stay in flight across it. For data the waves exchange through
+// LDS written with ds_* stores (copies into LDS by global_load_lds are counted
+// by vmcnt and need wait_vm_lds).
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Partial tiles cross workgroups (and L2 slices): agent-scope relaxed atomics
 // read and write them at the device-coherent level, so no cache flush or
 // invalidate is needed; a wait for the stores' completion orders them before

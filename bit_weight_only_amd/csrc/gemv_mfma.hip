@@ -173,10 +173,14 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
   constexpr int kEarly = DEPTH < 2 ? DEPTH : 2;
   const bool rotating = wv * 8 < units;   // wave-uniform: the wave's first unit exists
   MxItem<BITS> ring[DEPTH];
-  uint4 mv0;
+  // each thread's first two meta vectors go out with the activations; any
+  // further ones (none at the usual shapes) are loaded and stored on the spot
+  const bool two_meta = n_meta > static_cast<int>(blockDim.x);   // workgroup-uniform
+  uint4 mv0, mv1 = make_uint4(0, 0, 0, 0);
   if (rotating) {
     const RotIn rin = rot_load(xrs, srs, K, m0, u0 - m0 * G, rL, u0 < units);
     mv0 = meta_load(static_cast<int>(threadIdx.x));
+    if (two_meta) mv1 = meta_load(static_cast<int>(threadIdx.x + blockDim.x));
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -200,6 +204,7 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
     }
   } else {
     mv0 = meta_load(static_cast<int>(threadIdx.x));
+    if (two_meta) mv1 = meta_load(static_cast<int>(threadIdx.x + blockDim.x));
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -210,7 +215,8 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
     }
   }
   if (static_cast<int>(threadIdx.x) < n_meta) meta_store(static_cast<int>(threadIdx.x), mv0);
-  for (int i = static_cast<int>(threadIdx.x + blockDim.x); i < n_meta; i += static_cast<int>(blockDim.x))
+  if (static_cast<int>(threadIdx.x + blockDim.x) < n_meta) meta_store(static_cast<int>(threadIdx.x + blockDim.x), mv1);
+  for (int i = static_cast<int>(threadIdx.x + 2 * blockDim.x); i < n_meta; i += static_cast<int>(blockDim.x))
     meta_store(i, meta_load(i));
   {   // zero the padding groups' pieces and sums, every set's zero piece, the row sums
     const int pad = (Gp - G) * M;
@@ -229,7 +235,7 @@ __global__ void __launch_bounds__(kMxMaxThreads) gemv_mfma_kernel(const uint4 *_
     }
     for (int i = static_cast<int>(threadIdx.x); i < nw * M * rows; i += static_cast<int>(blockDim.x)) yl[i] = 0.f;
   }
-  __syncthreads();
+  barrier_lds();   // the ring's code loads stay in flight
 
   // A operand source of this lane: row i = lane & 15 holds piece i & 3 of token
   // i >> 2; rows of tokens >= M read token 0's zero piece

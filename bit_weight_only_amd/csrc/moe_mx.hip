@@ -236,7 +236,7 @@ __device__ void expert_linear(const MoeMxArgs &a, int e, int b, uint32_t *smem) 
             make_uint4(0, 0, 0, 0);
       }
     }
-    __syncthreads();
+    barrier_lds();   // the ring's code loads stay in flight
 
     // A operand source of this lane: row i = lane & 15 holds piece i & 3 of token
     // i >> 2; rows of tokens >= M read token 0's zero piece

@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(kPvqMaxThreads) gemv_pvq_mx_kernel(const uint4
     }
     for (int i = static_cast<int>(threadIdx.x); i < nw * M * vrows; i += nt) yl[i] = 0.f;
   }
-  __syncthreads();
+  barrier_lds();   // the ring's index loads stay in flight
 
   // A operand source of this lane: row i = lane & 15 holds piece i & 3 of token
   // i >> 2; rows of tokens >= M read token 0's zero piece (any scale)
