@@ -45,10 +45,15 @@ def oracle_rows(w, s, cb, stages, x, rows=None):
 @pytest.mark.parametrize("n,k", [(17, 512), (130, 1024), (257, 640)])
 @pytest.mark.parametrize("m,path", [(1, 0), (3, 0), (4, 1), (1, 2), (5, 0), (16, 0), (64, 0)])
 def test_pvq_stages_small(L, dev, bits, n, k, m, path):
-    if path == 1 and k % 512:
-        pytest.skip("the forced GEMV needs K a multiple of 512 at more than one stage")
     w, s, cb, idx, sc, pl = make(L, n, k, bits, n + k)
     x = synth.activations(m, k, workload=80, item=m)
+    if path == 1 and k % 512:
+        # residual stages run on the matrix-core GEMV (K a multiple of 512) or
+        # the GEMM only: a forced GEMV elsewhere is refused before any launch
+        with pytest.raises(L.LbqError) as err:
+            L.linear_forward(pl, to_dev(x, dev), path=path)
+        assert err.value.status == -2
+        return
     y = L.linear_forward(pl, to_dev(x, dev), path=path).cpu().numpy().astype(np.float64)
     e = O.rel_l2(y, oracle_rows(w, s, cb, bits // 2, x))
     say(f"pvq stages bits={bits} n={n} k={k} m={m} path={path}: rel_l2 {e:.3e}")
