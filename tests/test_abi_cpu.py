@@ -204,6 +204,21 @@ def test_workspace_queries(L):
     assert b.value >= 16 * 4096 * 2 and b.value % 256 == 0
     assert lib.lbq_linear_workspace(ctypes.byref(w), -1, ctypes.byref(b)) == -2
     assert lib.lbq_linear_workspace(ctypes.byref(w), 1, None) == -1
+    # zero tokens: nothing to plan
+    assert lib.lbq_linear_workspace(ctypes.byref(w), 0, ctypes.byref(b)) == 0
+
+
+def test_workspace_covers_every_gemm_plan(L):
+    """The workspace query sizes the MFMA GEMM's split-K partial tiles and
+    arrival counters from the plan for every token count (no plan for zero
+    tokens): at least the rotated activations, in 256-byte multiples."""
+    lib = L.lib()
+    b = ctypes.c_size_t()
+    for K, N in [(4096, 6144), (5120, 17408), (17408, 5120), (14336, 4096), (512, 17)]:
+        w = _w(L, K=K, N=N)
+        for M in [0, 1, 4, 5, 16, 17, 33, 64, 100, 256, 2048]:
+            assert lib.lbq_linear_workspace(ctypes.byref(w), M, ctypes.byref(b)) == 0
+            assert b.value >= M * K * 2 and b.value % 256 == 0, (K, N, M, b.value)
 
 
 def _moe(L, E=256, hidden=2048, ffn=1024, top_k=8, **kw):
