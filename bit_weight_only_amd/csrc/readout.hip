@@ -39,50 +39,22 @@ __device__ __forceinline__ uint64_t make_key(uint32_t k16, uint32_t row) {
   return (static_cast<uint64_t>(k16 + 1) << 32) | (0xFFFFFFFFu - row);
 }
 
-// The value of lane l ^ STRIDE, without the LDS crossbar (a ds_bpermute costs
-// a round trip through the LDS unit; these are register moves): DPP quad
-// permutes for 1 and 2, row shifts for 4, a row rotate for 8, and the
-// v_permlane16/32_swap exchanges between 16-lane rows and 32-lane halves.
-template <int STRIDE>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-  const int iv = static_cast<int>(v);
-  if constexpr (STRIDE == 1) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true));   // quad_perm [1, 0, 3, 2]
-  } else if constexpr (STRIDE == 2) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true));   // quad_perm [2, 3, 0, 1]
-  } else if constexpr (STRIDE == 4) {
-    const int up = __builtin_amdgcn_mov_dpp(iv, 0x104, 0xF, 0xF, true);   // row_shl:4: lane l + 4
-    const int dn = __builtin_amdgcn_mov_dpp(iv, 0x114, 0xF, 0xF, true);   // row_shr:4: lane l - 4
-    return static_cast<uint32_t>((lane & 4) ? dn : up);
-  } else if constexpr (STRIDE == 8) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true));  // row_ror:8
-  } else if constexpr (STRIDE == 16) {
-    // odd 16-lane rows of the first operand trade places with even rows of the
-    // second: with both v, the first result holds row r ^ 1 in odd rows and the
-    // second in even rows
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return ((lane >> 4) & 1) ? r[0] : r[1];
-  } else {
-    static_assert(STRIDE == 32, "stride");
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (lane & 32) ? r[0] : r[1];
-  }
-}
+// Lane exchanges go through xor_lane_u32 (DPP moves and permlane swaps): a
+// ds_bpermute would cost a round trip through the LDS unit per step.
 template <int STRIDE>
 __device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
-  const uint32_t lo = xor_lane<STRIDE>(static_cast<uint32_t>(v));
-  const uint32_t hi = xor_lane<STRIDE>(static_cast<uint32_t>(v >> 32));
+  const uint32_t lo = xor_lane_u32<STRIDE>(static_cast<uint32_t>(v));
+  const uint32_t hi = xor_lane_u32<STRIDE>(static_cast<uint32_t>(v >> 32));
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 // Sum over the wave's 64 lanes, in every lane (xor butterfly, fixed order).
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  v += xor_lane<32>(v);
-  v += xor_lane<16>(v);
-  v += xor_lane<8>(v);
-  v += xor_lane<4>(v);
-  v += xor_lane<2>(v);
-  v += xor_lane<1>(v);
+  v += xor_lane_u32<32>(v);
+  v += xor_lane_u32<16>(v);
+  v += xor_lane_u32<8>(v);
+  v += xor_lane_u32<4>(v);
+  v += xor_lane_u32<2>(v);
+  v += xor_lane_u32<1>(v);
   return v;
 }
 
@@ -330,12 +302,12 @@ __global__ void __launch_bounds__(256) refine_kernel(const uint64_t *__restrict_
       acc += s * (dot - z * xs);
     }
   }
-  acc += __builtin_bit_cast(float, xor_lane<32>(__builtin_bit_cast(uint32_t, acc)));
-  acc += __builtin_bit_cast(float, xor_lane<16>(__builtin_bit_cast(uint32_t, acc)));
-  acc += __builtin_bit_cast(float, xor_lane<8>(__builtin_bit_cast(uint32_t, acc)));
-  acc += __builtin_bit_cast(float, xor_lane<4>(__builtin_bit_cast(uint32_t, acc)));
-  acc += __builtin_bit_cast(float, xor_lane<2>(__builtin_bit_cast(uint32_t, acc)));
-  acc += __builtin_bit_cast(float, xor_lane<1>(__builtin_bit_cast(uint32_t, acc)));
+  acc += __builtin_bit_cast(float, xor_lane_u32<32>(__builtin_bit_cast(uint32_t, acc)));
+  acc += __builtin_bit_cast(float, xor_lane_u32<16>(__builtin_bit_cast(uint32_t, acc)));
+  acc += __builtin_bit_cast(float, xor_lane_u32<8>(__builtin_bit_cast(uint32_t, acc)));
+  acc += __builtin_bit_cast(float, xor_lane_u32<4>(__builtin_bit_cast(uint32_t, acc)));
+  acc += __builtin_bit_cast(float, xor_lane_u32<2>(__builtin_bit_cast(uint32_t, acc)));
+  acc += __builtin_bit_cast(float, xor_lane_u32<1>(__builtin_bit_cast(uint32_t, acc)));
   if (lane == 0) {
     ids[item] = row;
     logits[item] = acc;
