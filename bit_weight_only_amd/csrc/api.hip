@@ -66,8 +66,13 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return LBQ_ERR_ALIGN;
   if (ws_bytes < linear_ws_bytes(w, M)) return LBQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // up to four tokens share one matrix-core GEMV pass; from there on the MFMA GEMM
-  bool gemv = (path == LBQ_PATH_GEMV) || (path == LBQ_PATH_AUTO && M <= 4);
+  // up to four tokens share one matrix-core GEMV pass; from there on the MFMA
+  // GEMM, and also where the GEMV would need a second pass over the codes (three
+  // or four tokens on long rows: 14336 -> 4096 at four tokens 17.4 -> 15.0 us)
+  bool gemv = (path == LBQ_PATH_GEMV) ||
+              (path == LBQ_PATH_AUTO && M <= 4 &&
+               (w->format != LBQ_FMT_RTN_PLANES || !gemv_mfma_supported(M, w->K, w->N) ||
+                gemv_mfma_one_pass(M, w->K, w->N, w->bits)));
   // One to four tokens: rotation fused into the matrix-core decoder, one launch.
   if (w->format == LBQ_FMT_RTN_PLANES && gemv && gemv_mfma_supported(M, w->K, w->N) && aligned16(w->signs) &&
       (w->bits != 8 || gemv_mfma_supported_8bit(w->K, w->N)))

@@ -443,6 +443,13 @@ void gemv_mfma_shape(int M, int K, int N, int bits, int &grid, int &block, int &
   depth = bits == 3 ? 2 : (bits >= 4 || T >= 4 * kComputeUnits || G >= 64) ? 3 : 2;
 }
 
+bool gemv_mfma_one_pass(int M, int K, int N, int bits) {
+  int grid, block, depth;
+  gemv_mfma_shape(M, K, N, bits, grid, block, depth);
+  const int G = K / kGroup, T = (N + 15) / 16;
+  return tokens_per_pass(M, G, padded_groups(G, bits), ((T + grid - 1) / grid) * 16, block / 64) == M;
+}
+
 bool gemv_mfma_supported_8bit(int K, int N) {
   // buffer offsets are 32-bit and kOutOfRange must lie past the planes of 8-bit codes
   return static_cast<long long>(N + 16) * (K / kGroup) * 8 * 16 < static_cast<long long>(kOutOfRange);

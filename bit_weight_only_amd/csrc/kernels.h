@@ -51,6 +51,9 @@ hipError_t launch_gemv_rtn(const void *planes, const void *meta, const uint16_t 
 // take the kernel's own begin / end times.
 bool gemv_mfma_supported(int M, int K, int N);
 bool gemv_mfma_supported_8bit(int K, int N);   // the extra bound for 8-bit codes
+// true when all M tokens' activation pieces fit in LDS at once (else the
+// kernel runs the tokens in passes that each stream the codes again)
+bool gemv_mfma_one_pass(int M, int K, int N, int bits);
 void gemv_mfma_shape(int M, int K, int N, int bits, int &grid, int &block, int &depth);
 hipError_t launch_gemv_mfma(const void *planes, const void *meta, const uint16_t *x, const int8_t *signs,
                             uint16_t *y, int M, int K, int N, int bits, int grid, int block, int depth,

@@ -87,7 +87,9 @@ typedef enum {
 } lbq_format;
 
 /* Kernel path for lbq_linear_forward_path. AUTO picks the GEMV for M <= 4 and
- * the MFMA GEMM above (measured crossover); forcing the GEMV needs M <= 16.
+ * the MFMA GEMM above (measured crossover), and the GEMM also where the RTN
+ * matrix-core GEMV would run its tokens in two passes over the codes (three or
+ * four tokens on long rows); forcing the GEMV needs M <= 16.
  * LBQ_PATH_SPLIT_ROTATION may be OR-ed into any of them (for tests): the
  * GEMM's separate rotation launch then goes in launches of at most three
  * tokens each, the split it otherwise makes only past 1 GiB of activations. */
@@ -212,7 +214,9 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
  * Paths (AUTO):
  *   - M <= 4, K a multiple of 512, signs 16-byte aligned (PVQ: codebook 4-byte
  *     aligned): one launch, the matrix-core GEMV with the rotation in its
- *     prologue (nothing is written to ws);
+ *     prologue (nothing is written to ws), unless for RTN codes the tokens'
+ *     activation pieces do not all fit in LDS at once (three or four tokens on
+ *     long rows): then the MFMA GEMM as for M >= 5;
  *   - other M <= 4: a rotation launch into ws, then the staged VALU GEMV
  *     (8-bit codes and multi-stage PVQ: the MFMA GEMM instead; a forced GEMV
  *     that the matrix-core GEMV cannot take returns LBQ_ERR_SHAPE for them);

@@ -89,11 +89,13 @@ def test_gemv_matrix_core_tokens(L, dev, bits, n, k, m):
     """One to four tokens with K a multiple of 512 run the matrix-core GEMV
     (fp8 activation pieces x fp4 codes, rotation in the prologue): ragged N,
     fewer tiles than workgroups (n = 17, 300), more (n = 4100, 257 tiles),
-    long rows (K = 16384, 128 groups), every token count it serves."""
+    long rows (K = 16384, 128 groups: three and four tokens go in two passes),
+    every token count it serves. Forced GEMV path: AUTO sends the two-pass
+    cases to the GEMM."""
     say(f"gemv mfma bits={bits} n={n} k={k} m={m}")
     w, s, planes, meta, pl = make_rtn(n, k, bits, 17, n + k + bits)
     x = synth.activations(m, k, workload=17, item=m)
-    y = L.linear_forward(pl, to_dev(x, dev)).cpu().numpy().astype(np.float64)
+    y = L.linear_forward(pl, to_dev(x, dev), path=L.PATH_GEMV).cpu().numpy().astype(np.float64)
     rows = np.arange(n) if n <= 1100 else sample_rows(n, 48, seed=m)
     want = oracle_rtn_rows(w, s, bits, x, rows)
     assert O.rel_l2(y[:, rows], want) < TOL
@@ -322,3 +324,18 @@ def test_pvq_fp4_valued_codebook(L, dev, n, k, m, path):
     x = synth.activations(m, k, workload=16, item=500 + m)
     y = L.linear_forward(pl, to_dev(x, dev), path=path).cpu().numpy().astype(np.float64)
     assert O.rel_l2(y, oracle_pvq_rows(w, s, cb, x)) < TOL
+
+
+def test_auto_path_sends_two_pass_tokens_to_the_gemm(L, dev):
+    """At four tokens on 14336-long rows the matrix-core GEMV would run two
+    passes over the codes; AUTO takes the MFMA GEMM there (bit-identical to the
+    forced GEMM path) and keeps the one-pass GEMV at one token (bit-identical
+    to the forced GEMV path)."""
+    n, k = 256, 14336
+    w, s, planes, meta, pl = make_rtn(n, k, 2, 24, 0)
+    for m, forced in [(4, L.PATH_GEMM), (1, L.PATH_GEMV)]:
+        x = to_dev(synth.activations(m, k, workload=24, item=m), dev)
+        a = L.linear_forward(pl, x).cpu().numpy()
+        b = L.linear_forward(pl, x, path=forced).cpu().numpy()
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), m
+        assert O.rel_l2(a.astype(np.float64), oracle_rtn_rows(w, s, 2, x.cpu().numpy())) < TOL
