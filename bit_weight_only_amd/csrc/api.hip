@@ -2,6 +2,7 @@
 // and kernel launches on the caller's stream. No allocation, no global state.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -44,11 +45,26 @@ size_t tz_bytes(const lbq_weight *w, int M) {
   return w->format == LBQ_FMT_RTN_PLANES ? round_up(static_cast<size_t>(M) * gemm_tz_stride(w->K) * 4, kAlign) : 0;
 }
 
+// Up to 16 tokens of 2-bit RTN codes may run on the matrix-core GEMM (fp4
+// codes x e4m3 activation pieces).
+constexpr int kMxMaxTokens = 16;
+bool mx_possible(const lbq_weight *w, int M) {
+  return w->format == LBQ_FMT_RTN_PLANES && M >= 1 && M <= kMxMaxTokens && gemm_mx_supported(M, w->K, w->N, w->bits);
+}
+
+size_t act_bytes(const lbq_weight *w, int M) {
+  size_t b = round_up(static_cast<size_t>(M) * w->K * 2, kAlign);
+  if (mx_possible(w, M)) b = std::max(b, round_up(gemm_mx_act_bytes(M, w->K), kAlign));
+  return b;
+}
+
 size_t linear_ws_bytes(const lbq_weight *w, int M) {
-  // the rotated activations, the RTN GEMM's per-(token, group) sums, then the
-  // GEMM's split-K partial tiles and counters
-  return round_up(static_cast<size_t>(M) * w->K * 2, kAlign) + tz_bytes(w, M) +
-         gemm_scratch_bytes(linear_gemm_plan(w, M));
+  // the rotated activations (or the matrix-core GEMM's pieces and scale bytes),
+  // the RTN GEMMs' per-(token, group) sums, then the GEMM's split-K partial
+  // tiles and counters (the larger of the two GEMMs' plans)
+  size_t scratch = gemm_scratch_bytes(linear_gemm_plan(w, M));
+  if (mx_possible(w, M)) scratch = std::max(scratch, gemm_scratch_bytes(gemm_mx_plan(M, w->K, w->N)));
+  return act_bytes(w, M) + tz_bytes(w, M) + scratch;
 }
 
 lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint16_t *y, void *ws, size_t ws_bytes,
@@ -59,13 +75,30 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
   // test flag: the GEMM's rotation in launches of at most three tokens
   const int rot_tokens = (path & LBQ_PATH_SPLIT_ROTATION) ? 3 : 0;
   path &= ~LBQ_PATH_SPLIT_ROTATION;
-  if (path < LBQ_PATH_AUTO || path > LBQ_PATH_GEMM) return LBQ_ERR_SHAPE;
-  if (path == LBQ_PATH_GEMV && M > 16) return LBQ_ERR_SHAPE;
+  if (path < LBQ_PATH_AUTO || path > LBQ_PATH_GEMM_MX) return LBQ_ERR_SHAPE;
+  if ((path == LBQ_PATH_GEMV || path == LBQ_PATH_GEMM_MX) && M > 16) return LBQ_ERR_SHAPE;
   if (M == 0) return LBQ_OK;
+  if (path == LBQ_PATH_GEMM_MX && !mx_possible(w, M)) return LBQ_ERR_SHAPE;
   if (!x || !y || !ws) return LBQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return LBQ_ERR_ALIGN;
+  if (path == LBQ_PATH_GEMM_MX && !aligned16(w->signs)) return LBQ_ERR_ALIGN;
   if (ws_bytes < linear_ws_bytes(w, M)) return LBQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // The matrix-core GEMM for five to sixteen tokens of 2-bit codes, on request
+  // only: per launch it beat the fp16 GEMM on the smaller dense-stack shapes at
+  // 16 tokens (4096 -> 6144 8.8 -> 8.4 us, 4096 -> 4096 8.6 -> 7.4 us) but not
+  // on the larger ones (4096 -> 28672 15.9 -> 18.9 us, 14336 -> 4096 12.6 ->
+  // 16.5 us), and its rotation launch costs about 0.8 us more, so the stack as
+  // a whole measured no faster (57.5 against 56.3 us per layer)
+  if (path == LBQ_PATH_GEMM_MX) {
+    const GemmPlan gp = gemm_mx_plan(M, w->K, w->N);
+    uint8_t *tz = static_cast<uint8_t *>(ws) + act_bytes(w, M);
+    void *scratch = tz + tz_bytes(w, M);
+    if (launch_gemm_mx(gp, w->planes, w->meta, x, w->signs, ws, reinterpret_cast<uint32_t *>(tz), y, M, w->K, w->N,
+                       scratch, s, ev0) != hipSuccess)
+      return LBQ_ERR_HIP;
+    return (ev1 && hipEventRecord(ev1, s) != hipSuccess) ? LBQ_ERR_HIP : LBQ_OK;
+  }
   // up to four tokens share one matrix-core GEMV pass; from there on the MFMA
   // GEMM, and also where the GEMV would need a second pass over the codes (three
   // or four tokens on long rows: 14336 -> 4096 at four tokens 17.4 -> 15.0 us)
@@ -101,7 +134,7 @@ lbq_status forward_impl(const lbq_weight *w, const uint16_t *x, int32_t M, uint1
     const bool rtn = w->format == LBQ_FMT_RTN_PLANES;
     if (rtn && !gemm_rtn_supported(w->K, w->N, w->bits)) return LBQ_ERR_SHAPE;
     const GemmPlan gp = linear_gemm_plan(w, M);
-    uint8_t *after_x = static_cast<uint8_t *>(ws) + round_up(static_cast<size_t>(M) * w->K * 2, kAlign);
+    uint8_t *after_x = static_cast<uint8_t *>(ws) + act_bytes(w, M);
     uint32_t *tz = rtn ? reinterpret_cast<uint32_t *>(after_x) : nullptr;
     void *scratch = after_x + tz_bytes(w, M);
     // (the RTN GEMM takes the folded slot order, the product-VQ GEMM natural order)

@@ -115,6 +115,18 @@ struct GroupedGemm {
   float *out;
 };
 hipError_t launch_gemm_rtn_grouped(const GroupedGemm &g, hipStream_t s);
+// Matrix-core GEMM for 2-bit RTN codes at up to 16 tokens per token tile
+// (fp4 codes x three e4m3 activation pieces): a rotation launch writes the
+// pieces and scale bytes to act (gemm_mx_act_bytes(M, K) bytes), the
+// zero-point sums to tz ([M][gemm_tz_stride(K)] u32) and clears the split-K
+// counters in scratch, then the GEMM (a non-null `between` is recorded after
+// the rotation launch).
+bool gemm_mx_supported(int M, int K, int N, int bits);
+GemmPlan gemm_mx_plan(int M, int K, int N);
+size_t gemm_mx_act_bytes(int M, int K);
+hipError_t launch_gemm_mx(const GemmPlan &p, const void *planes, const void *meta, const uint16_t *x,
+                          const int8_t *signs, void *act, uint32_t *tz, uint16_t *y, int M, int K, int N,
+                          void *scratch, hipStream_t s, hipEvent_t between = nullptr);
 hipError_t launch_gemm_pvq(const GemmPlan &p, const void *idx, const void *row_scale, const uint8_t *codebook,
                            const uint16_t *xf, uint16_t *y, int M, int K, int N, int stages, void *scratch,
                            hipStream_t s);

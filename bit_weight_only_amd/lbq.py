@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("LBQ_LIBRARY") or os.path.join(_HERE, "liblbq.so")
 
 FMT_RTN_PLANES = 0
 FMT_PVQ_4x8 = 1
-PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_GEMM_MX = 0, 1, 2, 3
 PATH_SPLIT_ROTATION = 0x100   # test flag: the GEMM's rotation in launches of <= 3 tokens
 
 STATUS = {

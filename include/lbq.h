@@ -90,6 +90,12 @@ typedef enum {
  * the MFMA GEMM above (measured crossover), and the GEMM also where the RTN
  * matrix-core GEMV would run its tokens in two passes over the codes (three or
  * four tokens on long rows); forcing the GEMV needs M <= 16.
+ * LBQ_PATH_GEMM_MX (2-bit RTN codes, M <= 16, K a multiple of 512,
+ * 16-byte-aligned signs) runs the matrix-core GEMM: fp4 codes times three e4m3
+ * pieces per rotated activation (about twelve significant bits, as in the
+ * matrix-core GEMV), the scale applied in fp32 per group. AUTO does not take
+ * it (it measured no faster end to end than the fp16 GEMM); forcing it
+ * elsewhere returns LBQ_ERR_SHAPE (LBQ_ERR_ALIGN for unaligned signs).
  * LBQ_PATH_SPLIT_ROTATION may be OR-ed into any of them (for tests): the
  * GEMM's separate rotation launch then goes in launches of at most three
  * tokens each, the split it otherwise makes only past 1 GiB of activations. */
@@ -97,6 +103,7 @@ typedef enum {
   LBQ_PATH_AUTO = 0,
   LBQ_PATH_GEMV = 1,
   LBQ_PATH_GEMM = 2,
+  LBQ_PATH_GEMM_MX = 3,
   LBQ_PATH_SPLIT_ROTATION = 0x100
 } lbq_path;
 
@@ -198,9 +205,11 @@ lbq_status lbq_gptq_factor(const double *H, int32_t K, const int8_t *signs, doub
 lbq_status lbq_pack_gptq(const float *W, int32_t K, int32_t N, int32_t bits, const int8_t *signs,
                          const double *U, void *planes_out, void *meta_out);
 
-/* Workspace bytes lbq_linear_forward needs for M tokens (host query; the
- * rotated activations, the GEMM's zero-point sums and its split-K partial
- * tiles and counters). Errors as lbq_linear_forward's argument checks. */
+/* Workspace bytes lbq_linear_forward needs for M tokens on any path (host
+ * query; the rotated activations, or for 2-bit codes at M <= 16 the larger
+ * e4m3 pieces of LBQ_PATH_GEMM_MX, the GEMM's zero-point sums and its split-K
+ * partial tiles and counters). Errors as lbq_linear_forward's argument
+ * checks. */
 lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
 
 /* y[M][N] (fp16) = x[M][K] (fp16) W_hat^T, W_hat the weight w decodes to:
@@ -222,7 +231,7 @@ lbq_status lbq_linear_workspace(const lbq_weight *w, int32_t M, size_t *bytes);
  *     that the matrix-core GEMV cannot take returns LBQ_ERR_SHAPE for them);
  *   - M >= 5: a rotation launch into ws (for RTN in the GEMM's folded
  *     order, with the zero-point sums), then the MFMA dequant-GEMM.
- * Accumulation is fp32; the GEMM rounds each decoded RTN weight s q to fp16
+ * Accumulation is fp32; the fp16 GEMM rounds each decoded RTN weight s q to fp16
  * (the zero-point term s z sum_k x'_k is added separately), and each decoded
  * multi-stage PVQ weight to one fp16 value in units of stage 1's row scale. The RTN GEMM needs
  * N*K*b/8 < 2^31 - 4096 (LBQ_ERR_SHAPE otherwise). The result of a call does
@@ -233,8 +242,11 @@ lbq_status lbq_linear_forward(const lbq_weight *w, const uint16_t *x, int32_t M,
                               uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 
 /* lbq_linear_forward with an explicit kernel path (lbq_path, optionally with
- * LBQ_PATH_SPLIT_ROTATION): LBQ_PATH_GEMV (M <= 16, LBQ_ERR_SHAPE above) or
- * LBQ_PATH_GEMM (any M). The same operation and arguments; for tests that
+ * LBQ_PATH_SPLIT_ROTATION): LBQ_PATH_GEMV (M <= 16, LBQ_ERR_SHAPE above),
+ * LBQ_PATH_GEMM (any M) or LBQ_PATH_GEMM_MX (2-bit RTN, M <= 16, K a multiple
+ * of 512; LBQ_ERR_SHAPE otherwise: a rotation launch writing the e4m3 pieces,
+ * a power-of-two scale per (token, group) and the zero-point sums into ws,
+ * then the matrix-core GEMM). The same operation and arguments; for tests that
  * reach every kernel at shapes AUTO would send elsewhere. */
 lbq_status lbq_linear_forward_path(const lbq_weight *w, const uint16_t *x, int32_t M,
                                    uint16_t *y, void *ws, size_t ws_bytes, int32_t path,

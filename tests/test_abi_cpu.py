@@ -192,6 +192,14 @@ def test_linear_forward_argument_errors(L):
     assert _fwd(L, _w(L), ws_bytes=511) == -5
     assert _fwd(L, _w(L), M=17, path=1) == -2
     assert _fwd(L, _w(L), path=7) == -2
+    # the matrix-core GEMM path: 2-bit RTN, M <= 16, K a multiple of 512,
+    # 16-byte-aligned signs; refused before any launch otherwise
+    assert _fwd(L, _w(L, K=512), M=17, path=3) == -2
+    assert _fwd(L, _w(L, K=256), M=8, path=3) == -2
+    assert _fwd(L, _w(L, K=512, bits=3), M=8, path=3) == -2
+    assert _fwd(L, _w(L, K=512, fmt=1, cb=FAKE), M=8, path=3) == -2
+    assert _fwd(L, _w(L, K=512, signs=FAKE + 4), M=8, path=3) == -4
+    assert _fwd(L, _w(L, K=512), M=8, path=3, ws_bytes=1024) == -5
     # M = 0 is a valid no-op (returns before touching any pointer)
     assert _fwd(L, _w(L), M=0, x=0, y=0, ws=0) == 0
 
@@ -219,6 +227,9 @@ def test_workspace_covers_every_gemm_plan(L):
         for M in [0, 1, 4, 5, 16, 17, 33, 64, 100, 256, 2048]:
             assert lib.lbq_linear_workspace(ctypes.byref(w), M, ctypes.byref(b)) == 0
             assert b.value >= M * K * 2 and b.value % 256 == 0, (K, N, M, b.value)
+            if 1 <= M <= 16 and K % 512 == 0:
+                # room for the matrix-core GEMM's pieces: 16 token slots x K x 3 bytes
+                assert b.value >= 48 * K, (K, N, M, b.value)
 
 
 def _moe(L, E=256, hidden=2048, ffn=1024, top_k=8, **kw):
