@@ -94,6 +94,8 @@ KERNEL_SOURCES = {
                         "bit_weight_only_amd/csrc/device.h"],
     "gemm_pvq_kernel": ["bit_weight_only_amd/csrc/gemm.hip", "bit_weight_only_amd/csrc/gemm_common.h",
                         "bit_weight_only_amd/csrc/device.h"],
+    "gemm_mx_kernel": ["bit_weight_only_amd/csrc/gemm_mx.hip", "bit_weight_only_amd/csrc/mx_core.h",
+                       "bit_weight_only_amd/csrc/gemm_common.h", "bit_weight_only_amd/csrc/device.h"],
     "moe_mx_kernel": ["bit_weight_only_amd/csrc/moe_mx.hip", "bit_weight_only_amd/csrc/mx_core.h",
                       "bit_weight_only_amd/csrc/gemm_common.h", "bit_weight_only_amd/csrc/device.h"],
     "gemm_rtn_grouped_kernel": ["bit_weight_only_amd/csrc/gemm_rtn.hip", "bit_weight_only_amd/csrc/gemm_common.h",
@@ -227,8 +229,8 @@ def run_calls(lib, calls):
 class Stack:
     """Packed dense-stack weights, LAYERS device copies, and per-shape buffers."""
 
-    def __init__(self, L, torch, layers: int, M: int):
-        self.L, self.torch, self.layers, self.M = L, torch, layers, M
+    def __init__(self, L, torch, layers: int, M: int, path: int = 0):
+        self.L, self.torch, self.layers, self.M, self.path = L, torch, layers, M, path
         dev = torch.device("cuda:0")
         self.shapes = []
         for idx, (name, k, n) in enumerate(synth.DENSE_STACK_SHAPES):
@@ -245,6 +247,11 @@ class Stack:
         self.order = [(sh, sh["calls"][layer]) for layer in range(layers) for sh in self.shapes]
 
     def step(self, sp):
+        if self.path:   # an explicit kernel path (lbq_linear_forward_path)
+            fwd = self.lib.lbq_linear_forward_path
+            for sh, (w, x, M, y, ws, n) in self.order:
+                check(fwd(w, x, M, y, ws, n, self.path, sp), "lbq_linear_forward_path")
+            return
         fwd = self.lib.lbq_linear_forward
         for sh, (w, x, M, y, ws, n) in self.order:
             check(fwd(w, x, M, y, ws, n, sp), "lbq_linear_forward")
@@ -559,9 +566,9 @@ def extra_single(torch, L, steps):
     return r
 
 
-def extra_stack(torch, L, M, steps, layers=None):
+def extra_stack(torch, L, M, steps, layers=None, path=0):
     layers = layers or copies_for(stack_bytes(1))
-    st = Stack(L, torch, layers, M)
+    st = Stack(L, torch, layers, M, path)
     per_step = []
     t = time_graph(torch, st.step, steps, 2, per_step)
     per = t / steps
@@ -1059,13 +1066,15 @@ def planes_meta_bytes(k, n, bits):
 
 # ---------------------------------------------------------------- main
 
-CASES = ("stack1", "stack4", "stack16", "single", "ffn1", "ffn8", "ffn64", "ffn256", "pvq1", "pvq16", "pvq64", "moe",
+CASES = ("stack1", "stack4", "stack16", "stack16mx", "single", "ffn1", "ffn8", "ffn64", "ffn256", "pvq1", "pvq16", "pvq64", "moe",
          "moe256", "moe2048", "readout1", "readout4", "pvq6bpw1", "pvq6bpw16", "pvq6bpw64")
 
 
 def run_case(torch, L, case, steps):
     """One measurement alone (for rocprofv3 counter runs): prints its result."""
-    if case.startswith("stack"):
+    if case == "stack16mx":   # the dense stack at 16 tokens on the matrix-core GEMM (LBQ_PATH_GEMM_MX)
+        r = extra_stack(torch, L, 16, steps, path=L.PATH_GEMM_MX)
+    elif case.startswith("stack"):
         M = int(case[5:])
         r = extra_stack(torch, L, M, steps) if M > 1 else extra_stack(torch, L, 1, steps)
     elif case == "single":
