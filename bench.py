@@ -101,6 +101,8 @@ KERNEL_SOURCES = {
     "gemm_rtn_grouped_kernel": ["bit_weight_only_amd/csrc/gemm_rtn.hip", "bit_weight_only_amd/csrc/gemm_common.h",
                                 "bit_weight_only_amd/csrc/device.h"],
     "select_kernel": ["bit_weight_only_amd/csrc/readout.hip", "bit_weight_only_amd/csrc/device.h"],
+    "gemv_pvq_mx_kernel": ["bit_weight_only_amd/csrc/pvq_mx.hip", "bit_weight_only_amd/csrc/mx_core.h",
+                           "bit_weight_only_amd/csrc/gemm_common.h", "bit_weight_only_amd/csrc/device.h"],
 }
 
 
