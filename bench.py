@@ -1034,24 +1034,34 @@ def pmc_summary(case, kernel, out_path, dirs):
     print("\n".join(lines))
 
 
-def trace_table(trace_dir, out_path):
-    """Per-kernel durations of every part of the hot path, from a rocprofv3
-    kernel trace of the default bench command."""
+def trace_table(trace_dir, out_path, case=None):
+    """Per-kernel durations from a rocprofv3 kernel trace of the default bench
+    command (every part of the hot path), or of 'bench.py --case CASE'."""
     import csv
 
     stats = []
     for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
         stats += list(csv.DictReader(open(f)))
-    lines = [
-        "rocprofv3 kernel-trace statistics of the default bench command (all parts of the hot path:",
-        "dense stack at M=1, 4, 16; FFN pair at M=1, 8, 64, 256; product-VQ at M=1, 16, 64 at 2 and 6 bits",
-        "per weight; MoE block at M=32, 256, 2048; the screened 8-bit readout at M=1, 4; the streaming-read",
-        "floor; oracle timing on the host runs no GPU kernels).",
-        "",
-        "command (run from the repository root, cd /tmp && export TMPDIR=/tmp first):",
-        "  rocprofv3 --kernel-trace --stats -d <dir> -o k --output-format csv -- python3 bench.py",
-        "  python3 bench.py --trace-summary <dir> <this file>",
-        "",
+    if case:
+        lines = [f"rocprofv3 kernel-trace statistics of 'python3 bench.py --case {case} --steps 10' (the case's",
+                 "graph-replayed launches and its untimed warm-up and capture).",
+                 "",
+                 "command (run from the repository root, cd /tmp && export TMPDIR=/tmp first):",
+                 f"  rocprofv3 --kernel-trace --stats -d <dir> -o k --output-format csv -- python3 bench.py --case {case} --steps 10",
+                 f"  python3 bench.py --trace-summary <dir> <this file> {case}",
+                 ""]
+    else:
+        lines = [
+            "rocprofv3 kernel-trace statistics of the default bench command (all parts of the hot path:",
+            "dense stack at M=1, 4, 16; FFN pair at M=1, 8, 64, 256; product-VQ at M=1, 16, 64 at 2 and 6 bits",
+            "per weight; MoE block at M=32, 256, 2048; the screened 8-bit readout at M=1, 4; the streaming-read",
+            "floor; oracle timing on the host runs no GPU kernels).",
+            "",
+            "command (run from the repository root, cd /tmp && export TMPDIR=/tmp first):",
+            "  rocprofv3 --kernel-trace --stats -d <dir> -o k --output-format csv -- python3 bench.py",
+            "  python3 bench.py --trace-summary <dir> <this file>",
+            ""]
+    lines += [
         f"  {'kernel':130s} {'calls':>7s} {'avg us':>10s} {'min us':>9s} {'total us':>12s}",
     ]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
@@ -1108,9 +1118,10 @@ def main():
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                     help="write the counter summary under profiles/ from rocprofv3 outputs, then exit")
     ap.add_argument("--summary-command", default="python3 bench.py --steps 5 --warmup 1 --no-extra --no-cpu")
-    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "OUT"),
-                    help="write a per-kernel table of a rocprofv3 --kernel-trace --stats run of the default "
-                         "command (python3 bench.py) to OUT, then exit")
+    ap.add_argument("--trace-summary", nargs="+", metavar="ARG",
+                    help="TRACE_DIR OUT [CASE]: write a per-kernel table of a rocprofv3 --kernel-trace --stats "
+                         "run of the default command (python3 bench.py), or of 'bench.py --case CASE', to OUT, "
+                         "then exit")
     ap.add_argument("--pmc-summary", nargs="+", metavar="ARG",
                     help="CASE KERNEL OUT DIR...: counters of one kernel from rocprofv3 --pmc runs of "
                          "'bench.py --case CASE' (one directory per pass), written to OUT, then exit")
